@@ -1,0 +1,144 @@
+/*
+ * mla_decode.h — C ABI of the absorbed-MLA decode library for MI355X (gfx950).
+ *
+ * The operation.  In decode, absorbed Multi-head Latent Attention lets every
+ * query head, already projected into the latent space, attend directly over
+ * one shared latent per cached token (page "DP attention + expert parallel:
+ * MLA KV replication", section "A strong answer").  Per layer the cache is a
+ * paged array [NB, BS, 576] whose elements 0..511 are kv_c and 512..575 are
+ * k_rope; the 64 RoPE dimensions are shared by all heads MQA-style (page
+ * "MLA 的 TP 切分：为什么 8 张 GPU 存了同一份 KV cache", sections 一 and
+ * 3.1).  The value vector is the kv_c part, since the value head size equals
+ * kv_lora_rank (page "DP 与 DPA 的区别：SGLang 并行部署与路由", section
+ * "MLA：KV 是一份共享 latent，没有多个 head 可切").  For request b with
+ * L = seq_lens[b] cached tokens, token t lives in row
+ * latent_cache[block_table[b*M + t/BS], t%BS, :] and, for each head h,
+ *
+ *   s_t      = scale * sum_{d<576} q[b,h,d] * c_t[d]
+ *   out[b,h] = sum_t softmax_t(s)_t * c_t[0:512]            (bf16, RNE)
+ *   lse[b,h] = ln sum_t exp(s_t)                            (fp32)
+ *
+ * L = 0 gives out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library only borrows them for the work it enqueues on `stream`.
+ *   - Calls are asynchronous: they enqueue kernels on `stream` and return
+ *     without synchronising.  seq_lens is never read on the host.
+ *   - The library allocates no device memory.  Scratch (the work plan and
+ *     split-KV partial results) lives in a caller-provided workspace of at
+ *     least mla_decode_workspace_bytes(...) bytes, 256-byte aligned.
+ *   - Argument checks run on the host before any HIP call; a failed check
+ *     returns its status and enqueues nothing.  MLA_ERR_HIP reports a
+ *     launch failure (hipGetLastError after the launch).
+ *   - Data-dependent contract violations (seq_lens[b] < 0 or > M*BS, a used
+ *     block-table entry outside [0, NB)) never cause out-of-bounds accesses:
+ *     lengths are clamped to [0, M*BS] and bad block ids are replaced by 0.
+ *     The affected outputs are unspecified and a flag is raised in the
+ *     workspace (read it with mla_decode_read_error).
+ *   - Calls that share a workspace must be ordered (same stream, or
+ *     synchronised); concurrent calls need separate workspaces.
+ *   - Supported shapes: 1 <= H <= 128; BS a power of two in [16, 1024];
+ *     B >= 0 (B = 0 is a no-op); M >= 1; NB >= 1; M*BS <= 2^28.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q            bf16  [B, H, 576]    16-byte aligned
+ *   latent_cache bf16  [NB, BS, 576]  16-byte aligned
+ *   block_table  int32 [B, M]
+ *   seq_lens     int32 [B]
+ *   out          bf16  [B, H, 512]    16-byte aligned  (written)
+ *   lse          fp32  [B, H]         4-byte aligned   (written, natural log)
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
+  MLA_ERR_BAD_SHAPE = 2,    /* negative or overflowing sizes                      */
+  MLA_ERR_UNSUPPORTED = 3,  /* H, BS or chunk_tokens outside the supported set    */
+  MLA_ERR_BAD_SCALE = 4,    /* scale is not finite                                */
+  MLA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required         */
+  MLA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed         */
+  MLA_ERR_ALIGNMENT = 7     /* a pointer violates the alignment stated above      */
+} mla_status;
+
+/* Bits of the data-check word raised in the workspace (see mla_decode_read_error). */
+#define MLA_CHECK_SEQ_LEN_RANGE 1  /* some seq_lens[b] < 0 or > M*BS (clamped)       */
+#define MLA_CHECK_BLOCK_ID_RANGE 2 /* some used block id outside [0, NB) (set to 0)  */
+
+/* Bytes of workspace needed for a batch of B requests with H heads, a block
+ * table of M entries per request and block size BS.  Returns 0 when the sizes
+ * are outside the supported set.  The figure covers the work plan and fp32
+ * split-KV partials for at most B + 1024 work items. */
+size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS);
+
+/* Whole decode: plan, attend, merge — the three calls below in order.  The
+ * chunk size of the split-KV plan is chosen on the device from seq_lens. */
+mla_status mla_decode(const void* q, const void* latent_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, void* out, float* lse,
+                      int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 1 — split-KV work plan.  One small kernel reads seq_lens and writes
+ * into the workspace a list of work items (request, token range), each at
+ * most chunk_tokens long, ordered full chunks first.  chunk_tokens = 0 lets
+ * the device pick the chunk (a multiple of 32 tokens) that minimises an
+ * estimate of the makespan on this GPU's compute units; a positive value
+ * forces that chunk size (it must be a multiple of 32, and
+ * B * ceil(M*BS / chunk_tokens) must not exceed B + 1024).  The plan depends
+ * only on seq_lens, so one plan serves every layer of a decode step.
+ *
+ * Workspace layout written by the plan (int32 words unless noted):
+ *   [0] number of work items   [1] chunk tokens   [2] data-check bits
+ *   [3] work-queue counter (0 after the plan and after every attend call)
+ *   [4] number of full items
+ *   at byte 256: per request 4 words (first full item, full-item count,
+ *   remainder item or -1, total item count);
+ *   then per item 4 words (request, first token, end token, partial slot or
+ *   -1 when the item writes out/lse directly). */
+mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
+                           int32_t M, int32_t BS, int32_t chunk_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 2 — attention over each work item (the hot kernel).  For an item that
+ * covers a whole request it writes out/lse; otherwise it writes the item's
+ * normalised fp32 output and its log-sum-exp as a partial result into the
+ * workspace.  Needs a plan made with the same B, H, M, BS. */
+mla_status mla_decode_attend(const void* q, const void* latent_cache,
+                             const int32_t* block_table, float scale,
+                             void* out, float* lse,
+                             int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 3 — log-sum-exp merge of the partial results of every split request:
+ * lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s (bf16, RNE).
+ * Requests with no tokens get out = 0, lse = -inf.  Requests that were not
+ * split are left as step 2 wrote them. */
+mla_status mla_decode_merge(void* out, float* lse, int32_t B, int32_t H,
+                            int32_t M, int32_t BS,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream`, then copies the data-check word of the workspace
+ * into *flags (0 = no violation seen since the last plan). */
+mla_status mla_decode_read_error(const void* workspace, int32_t* flags, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(mla_status s);
+
+/* Library ABI version (increments on any signature change). */
+int32_t mla_decode_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,120 @@
+"""Absorbed-form MLA decode over a paged 576-wide latent cache, for MI355X.
+
+The computation runs in the HIP library ``libmla_decode.so`` (C ABI in
+``include/mla_decode.h``); this package only marshals torch tensors into it.
+PyTorch provides device memory and the current stream.
+
+    out, lse = decode(q, latent_cache, block_table, seq_lens, scale)
+
+q [B, H, 576] bf16, latent_cache [NB, BS, 576] bf16, block_table [B, M] int32,
+seq_lens [B] int32, all on the same GPU; returns out [B, H, 512] bf16 and
+lse [B, H] float32 (natural log).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MlaError  # noqa: F401
+
+__all__ = ["decode", "Workspace", "plan", "attend", "merge", "MlaError"]
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_inputs(q, cache, table, lens):
+    if not (q.is_cuda and cache.is_cuda and table.is_cuda and lens.is_cuda):
+        raise ValueError("all inputs must be GPU tensors")
+    if q.dtype != torch.bfloat16 or cache.dtype != torch.bfloat16:
+        raise TypeError("q and latent_cache must be bfloat16")
+    if table.dtype != torch.int32 or lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    if q.dim() != 3 or q.shape[2] != 576:
+        raise ValueError(f"q must be [B, H, 576], got {tuple(q.shape)}")
+    if cache.dim() != 3 or cache.shape[2] != 576:
+        raise ValueError(f"latent_cache must be [NB, BS, 576], got {tuple(cache.shape)}")
+    B = q.shape[0]
+    if table.dim() != 2 or table.shape[0] != B or lens.shape != (B,):
+        raise ValueError("block_table must be [B, M] and seq_lens [B]")
+    for t in (q, cache, table, lens):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+
+
+class Workspace:
+    """Device scratch for the plan and split partials, reusable across calls."""
+
+    def __init__(self, B: int, H: int, M: int, BS: int, device=None):
+        n = _lib.mla_decode_workspace_bytes(B, H, M, BS)
+        if n == 0:
+            raise ValueError(f"unsupported sizes B={B} H={H} M={M} BS={BS}")
+        self.shape = (B, H, M, BS)
+        self.nbytes = n
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def header(self) -> list:
+        """First words of the plan header: [n_items, chunk, check bits, queue, n_full]."""
+        return self.buf[:20].view(torch.int32).tolist()
+
+    def check_flags(self) -> int:
+        return _lib.mla_decode_read_error(self.ptr, _stream())
+
+
+def _ws(ws: Optional[Workspace], B, H, M, BS, device) -> Workspace:
+    if ws is None or ws.shape != (B, H, M, BS):
+        ws = Workspace(B, H, M, BS, device)
+    return ws
+
+
+def decode(q: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None
+           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Absorbed MLA decode of one layer (plan + attend + merge)."""
+    _check_inputs(q, latent_cache, block_table, seq_lens)
+    B, H, _ = q.shape
+    NB, BS, _ = latent_cache.shape
+    M = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws = _ws(workspace, B, H, M, BS, q.device)
+    st = _lib.mla_decode(q.data_ptr(), latent_cache.data_ptr(), block_table.data_ptr(),
+                         seq_lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
+                         B, H, NB, BS, M, ws.ptr, ws.nbytes, _stream())
+    _lib._check("mla_decode", st)
+    return out, lse
+
+
+def plan(seq_lens: torch.Tensor, H: int, M: int, BS: int, workspace: Workspace,
+         chunk_tokens: int = 0) -> None:
+    B = seq_lens.shape[0]
+    st = _lib.mla_decode_plan(seq_lens.data_ptr(), B, H, M, BS, chunk_tokens,
+                              workspace.ptr, workspace.nbytes, _stream())
+    _lib._check("mla_decode_plan", st)
+
+
+def attend(q, latent_cache, block_table, scale, out, lse, workspace: Workspace) -> None:
+    B, H, _ = q.shape
+    NB, BS, _ = latent_cache.shape
+    M = block_table.shape[1]
+    st = _lib.mla_decode_attend(q.data_ptr(), latent_cache.data_ptr(), block_table.data_ptr(),
+                                float(scale), out.data_ptr(), lse.data_ptr(), B, H, NB, BS, M,
+                                workspace.ptr, workspace.nbytes, _stream())
+    _lib._check("mla_decode_attend", st)
+
+
+def merge(out, lse, M: int, BS: int, workspace: Workspace) -> None:
+    B, H, _ = out.shape
+    st = _lib.mla_decode_merge(out.data_ptr(), lse.data_ptr(), B, H, M, BS, workspace.ptr,
+                               workspace.nbytes, _stream())
+    _lib._check("mla_decode_merge", st)

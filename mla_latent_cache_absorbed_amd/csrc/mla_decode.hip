@@ -1,0 +1,829 @@
+// Absorbed-MLA decode over a paged 576-wide bf16 latent cache, for gfx950.
+//
+// Three kernels behind the C ABI declared in include/mla_decode.h:
+//
+//   mla_plan_kernel    one workgroup: reads seq_lens, picks a split-KV chunk
+//                      size, writes the list of (request, token range) work
+//                      items into the workspace.
+//   mla_attend_kernel  the hot loop.  One workgroup per compute unit pulls
+//                      work items from a queue.  Each wave owns 32 heads.
+//                      Latent rows are streamed HBM -> LDS with direct-to-LDS
+//                      loads into a ring of 32-token stages; every staged row
+//                      is reused by all heads of the request.  Scores
+//                      S^T[token, head] = K * Q^T over all 576 dims and the
+//                      weighted sum O^T[col, head] += V^T * P^T over the 512
+//                      kv_c dims run on 32x32x16 bf16 MFMA with fp32
+//                      accumulation; the softmax is an fp32 online softmax in
+//                      the exp2 domain with a lazily moved running max.
+//   mla_merge_kernel   log-sum-exp merge of the partial results of split
+//                      requests.
+//
+// The operation: each head's absorbed query attends over the shared latent
+// directly (page "DP attention + expert parallel: MLA KV replication",
+// section "A strong answer"); scores use all 576 dims including the MQA-shared
+// k_rope (page "MLA 的 TP 切分…", section 一, and the first of page 1's
+// "Common mistakes"); the value is the kv_c half of the same row (page
+// "DP 与 DPA 的区别…", section "MLA：KV 是一份共享 latent…").
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "../../include/mla_decode.h"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// constants of the layout
+// ---------------------------------------------------------------------------
+constexpr int kD = 576;                   // latent width (kv_c 512 + k_rope 64)
+constexpr int kDV = 512;                  // value width (kv_c)
+constexpr int kSub = 32;                  // tokens per LDS stage
+constexpr int kRegionB = kSub * 64 * 16;  // byte offset of the k_rope region in a stage
+constexpr int kStageBytes = kSub * kD * 2;  // 36,864 B
+constexpr int kLoadsPerStage = kSub + 4;  // 1 KB direct-to-LDS loads per stage
+constexpr int kMaxExtraItems = 1024;      // work items beyond B the workspace holds
+constexpr int kHdrBytes = 256;
+constexpr float kRefHeadroom = 64.0f;     // log2 units: P <= 2^64 before an item is redone
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// Workspace sections (byte offsets).
+struct WsLayout {
+  size_t req_off, item_off, plse_off, po_off, total;
+  int cap;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline WsLayout ws_layout(int B, int H) {
+  WsLayout w;
+  w.cap = B + kMaxExtraItems;
+  w.req_off = kHdrBytes;
+  w.item_off = align256(w.req_off + size_t(B) * 16);
+  w.plse_off = align256(w.item_off + size_t(w.cap) * 16);
+  w.po_off = align256(w.plse_off + size_t(w.cap) * H * 4);
+  w.total = align256(w.po_off + size_t(w.cap) * H * kDV * 4);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// LDS stage layout and swizzles
+//
+// A stage holds 32 latent rows (36,864 B):
+//   region A, bytes [0, 32768): kv_c, row-major [token][64 chunks of 16 B];
+//             chunk c of token t sits at slot c ^ swzA(t) of row t.
+//   region B, bytes [32768, 36864): k_rope, chunk-major [8 chunks][32 tokens];
+//             chunk c' of token t at 32768 + 512 c' + 16 t.
+// Region A is filled one token row (1 KB, fully coalesced) per load.  Its
+// swizzle makes the MFMA operand reads bank-conflict free under both a
+// 128-byte and a 256-byte LDS line:
+//   QK reads : lanes 0..31 read tokens 0..31 at one chunk (16 B each);
+//   PV reads : ds_read_b64_tr_b16, each 16-lane group reads 4 consecutive
+//              tokens x 2 consecutive chunks x 2 halves (8 B each).
+// Region B is read only by QK: 32 consecutive tokens of one chunk are 512
+// contiguous bytes, so it needs no swizzle.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swzA(int t) {
+  const int t0 = t & 1, t1 = (t >> 1) & 1, t2 = (t >> 2) & 1, t3 = (t >> 3) & 1;
+  return ((t1 ^ t3) << 3) | (t0 << 2) | (t1 << 1) | t2;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  // s_waitcnt vmcnt(N) expcnt(7) lgkmcnt(0), gfx9 encoding.
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMAs of the hot loop are written out so that register classes are pinned:
+// the 16 output accumulators of a wave (32 heads x 512 columns, fp32) fill
+// all 256 AGPRs and the score accumulator lives in VGPRs.  Left to itself
+// the compiler gives every MFMA builtin of a kernel this size the AGPR form
+// and then spills.  Hazards the compiler cannot see through inline asm are
+// covered here: every MFMA is preceded by two wait states (a VALU write of an
+// operand just before it); back-to-back accumulation into the same
+// registers needs none; mfma_drain() provides >= 19 wait states between the
+// last XDL write of an accumulator and any non-MFMA access to it.
+__device__ __forceinline__ void qk_mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void pv_drain(f32x16 (&o)[16]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+}
+
+struct AttendArgs {
+  const __bf16* q;
+  const __bf16* cache;
+  const int32_t* table;
+  __bf16* out;
+  float* lse;
+  int32_t* hdr;          // workspace header (n_items, chunk, check bits, queue)
+  const int4* items;     // work items
+  float* part_lse;       // [cap, H]
+  float* part_o;         // [cap, H, 512]
+  float scale_log2;      // scale * log2(e)
+  int32_t B, H, NB, M, lgBS;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* cache, int blk,
+                                                             uint32_t blk_bytes) {
+  // raw buffer over one physical block; accesses past its end read zero
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(cache + size_t(blk) * blk_bytes), (short)0,
+                                           (int)blk_bytes, 0x00020000);
+}
+
+// Issue this wave's share of the direct-to-LDS loads of one stage (32/NW
+// region-A rows and 4/NW region-B loads).  Tokens past `t1` are clamped to
+// t1-1, a row of the request that is always valid; the softmax masks them.
+template <int NW>
+__device__ __forceinline__ void issue_stage(const AttendArgs& a, char LDS_AS* sbuf, int b,
+                                            int base, int t1, int w, int lane, int& bad) {
+  const int lg = a.lgBS;
+  const int bs_mask = (1 << lg) - 1;
+  const uint32_t blk_bytes = uint32_t(kD * 2) << lg;
+  const int32_t* trow = a.table + size_t(b) * a.M;
+  const int last = t1 - 1;
+  // base is a multiple of 32 and BS >= 16: at most two blocks per stage
+  const int lb0 = base >> lg;
+  const int lb1 = min(base + kSub - 1, last) >> lg;
+  int blk0 = trow[lb0];
+  int blk1 = trow[lb1];
+  if ((unsigned)blk0 >= (unsigned)a.NB) { blk0 = 0; bad = 1; }
+  if ((unsigned)blk1 >= (unsigned)a.NB) { blk1 = 0; bad = 1; }
+  const char* cbase = reinterpret_cast<const char*>(a.cache);
+  const __amdgpu_buffer_rsrc_t r0 = block_rsrc(cbase, blk0, blk_bytes);
+  const __amdgpu_buffer_rsrc_t r1 = block_rsrc(cbase, blk1, blk_bytes);
+  const uint32_t lane16 = uint32_t(lane) * 16;
+#pragma unroll
+  for (int k = 0; k < kSub / NW; ++k) {
+    const int i = w + NW * k;                 // region-A row, wave-uniform
+    const int tok = min(base + i, last);
+    const uint32_t voff = uint32_t(tok & bs_mask) * (kD * 2) + (lane16 ^ uint32_t(swzA(i) * 16));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(((tok >> lg) == lb0) ? r0 : r1, sbuf + i * 1024, 16,
+                                             voff, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 4 / NW; ++k) {
+    const int j = w + NW * k;                 // region-B load: chunks 2j, 2j+1
+    const int t = lane & 31;
+    const int cp = 2 * j + (lane >> 5);
+    const int tok = min(base + t, last);
+    const int blk = ((tok >> lg) == lb0) ? blk0 : blk1;
+    const size_t row = (size_t(blk) << lg) | size_t(tok & bs_mask);
+    const char* src = cbase + row * (kD * 2) + 1024 + cp * 16;
+    __builtin_amdgcn_global_load_lds(src, sbuf + kRegionB + j * 1024, 16, 0, 0);
+  }
+}
+
+template <int NW, int NS>
+__global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
+  static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
+  __shared__ __attribute__((aligned(1024))) char lds_raw[NS * kStageBytes];
+  __shared__ int s_item;
+  char LDS_AS* lds = (char LDS_AS*)(lds_raw);
+
+  constexpr int LPW = kLoadsPerStage / NW;  // loads per wave per stage
+  constexpr int PFK = 4;                    // QK operand reads in flight
+  constexpr int PFV = 4;                    // PV operand reads in flight
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int hl = lane & 31;
+  const int hi = lane >> 5;
+  const int head = w * 32 + hl;
+  const bool head_ok = head < a.H;
+  const int n_items = __builtin_amdgcn_readfirstlane(a.hdr[0]);
+
+  // Per-lane LDS offsets of the MFMA operand reads (relative to a stage).
+  // QK region A: k-step s = 8q + j reads chunk 2s + hi of token hl at
+  // qk_off[j] + 256 q.  QK region B: k-step 32 + jj at qkb + 1024 jj.
+  int qk_off[8];
+  {
+    const int xa = swzA(hl);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qk_off[j] = hl * 1024 + ((((2 * j) | hi)) ^ xa) * 16;
+  }
+  const int qkb = kRegionB + hi * 512 + hl * 16;
+  // PV transposed reads: lane reads token 16kk + 8e + 4hi + r, chunk 4cb + cc,
+  // half u0 (r = lane bits 3:2, cc = 2*bit4 + bit1, u0 = bit0) at
+  // pv_off[e][cb & 3] + 16384 kk + 256 (cb >> 2).
+  int pv_off[2][4];
+  {
+    const int r = (lane >> 2) & 3;
+    const int cc = (((lane >> 4) & 1) << 1) | ((lane >> 1) & 1);
+    const int u0 = lane & 1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int T = 8 * e + 4 * hi + r;
+      const int sa = swzA(T);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv_off[e][j] = T * 1024 + (((4 * j) | cc) ^ sa) * 16 + 8 * u0;
+    }
+  }
+
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[3], 1);
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    if (it >= n_items) {
+      // Every workgroup makes exactly one failing fetch; the last of them
+      // leaves the queue at 0 so that the same plan serves the next call.
+      if (threadIdx.x == 0 && it == n_items + int(gridDim.x) - 1) atomicExch(&a.hdr[3], 0);
+      break;
+    }
+
+    const int4 item = a.items[it];
+    const int b = __builtin_amdgcn_readfirstlane(item.x);
+    const int t0 = __builtin_amdgcn_readfirstlane(item.y);
+    const int t1 = __builtin_amdgcn_readfirstlane(item.z);
+    const int slot = __builtin_amdgcn_readfirstlane(item.w);
+    const int nst = (t1 - t0 + kSub - 1) / kSub;
+    int bad = 0;
+
+    // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
+    // lane holds head hl, dims 16s + 8hi .. +7.
+    bf16x8 qreg[36];
+    {
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+          a.q + (size_t(b) * a.H + (head_ok ? head : 0)) * kD + 8 * hi);
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        bf16x8 v = qp[2 * s];
+        if (!head_ok) v = bf16x8{};
+        qreg[s] = v;
+      }
+    }
+
+    // Prologue: stages 0 .. NS-2.
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nst) issue_stage<NW>(a, lds + p * kStageBytes, b, t0 + p * kSub, t1, w, lane, bad);
+
+    f32x16 o[16];
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+
+    // ---- stage pieces ----
+    // Scores S^T[token, head] over all 576 dims; lane holds head hl and
+    // tokens 8(v/4) + 4hi + (v%4) of the stage in sacc[v].
+    auto stage_scores = [&](const char LDS_AS* sb, f32x16& sacc) {
+      bf16x8 kf[PFK];
+#define MLA_KREAD(s)                                                                   \
+  ((s) < 32 ? *(const bf16x8 LDS_AS*)(sb + qk_off[(s) & 7] + 256 * ((s) >> 3))        \
+            : *(const bf16x8 LDS_AS*)(sb + qkb + 1024 * ((s) - 32)))
+#pragma unroll
+      for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(s);
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
+        else qk_mfma(sacc, kf[s % PFK], qreg[s]);
+        if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(s + PFK);
+      }
+#undef MLA_KREAD
+      qk_drain(sacc);
+    };
+    // Scale to the exp2 domain, mask tokens >= t1, return the per-head max.
+    auto stage_max = [&](f32x16& sacc, int base) -> float {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tk = base + 8 * (v >> 2) + 4 * hi + (v & 3);
+        const float x = (tk < t1) ? sacc[v] * a.scale_log2 : -INFINITY;
+        sacc[v] = x;
+        mx = fmaxf(mx, x);
+      }
+      return fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l^32 hold the same head
+    };
+    // P = exp2(S - m_run) (bf16 for the MFMA), row sums, and
+    // O^T[col, head] += V^T[col, token] * P^T[token, head].
+    auto stage_pv = [&](const char LDS_AS* sb, const f32x16& sacc) {
+      bf16x8 p0, p1;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[v] - m_run);
+        l_run += pv;
+        if (v < 8) p0[v] = (__bf16)pv;
+        else p1[v - 8] = (__bf16)pv;
+      }
+      // order n = 16 kk + cb: consecutive MFMAs use different accumulators
+      bf16x8 vf[PFV];
+#define MLA_VREAD(n, dst)                                                                   \
+  do {                                                                                      \
+    const int cb_ = (n) & 15, kk_ = (n) >> 4;                                               \
+    const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                        \
+    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
+        (bf16x4 LDS_AS*)(sb + pv_off[0][cb_ & 3] + imm_));                                  \
+    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
+        (bf16x4 LDS_AS*)(sb + pv_off[1][cb_ & 3] + imm_));                                  \
+    dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
+  } while (0)
+#pragma unroll
+      for (int n = 0; n < PFV; ++n) MLA_VREAD(n, vf[n]);
+#pragma unroll
+      for (int n = 0; n < 32; ++n) {
+        pv_mfma(o[n & 15], vf[n % PFV], (n >> 4) ? p1 : p0);
+        if (n + PFV < 32) MLA_VREAD(n + PFV, vf[n % PFV]);
+      }
+#undef MLA_VREAD
+    };
+
+    // ---- stage loop ----
+    // Each head's exponent reference m_run is fixed from the item's first
+    // stage (where O is still zero), so O is never rescaled: P = 2^(s - m_run)
+    // may grow up to 2^kRefHeadroom on later stages, which fp32 sums and bf16
+    // weights carry exactly in relative terms.  If a later score exceeds the
+    // reference by more than that (not seen with attention-like data), the
+    // whole item is redone with the larger reference.
+    float m_seen = -INFINITY;
+    for (;;) {
+      bool over = false;
+      for (int k = 0; k < nst; ++k) {
+        // Wait for this wave's loads of stage k; later stages may stay in flight.
+        if (k + NS - 2 < nst) wait_vmcnt_lgkm0<LPW * (NS - 2)>();
+        else wait_vmcnt_lgkm0<0>();
+        block_barrier();
+        if (k + NS - 1 < nst)
+          issue_stage<NW>(a, lds + ((k + NS - 1) % NS) * kStageBytes, b,
+                          t0 + (k + NS - 1) * kSub, t1, w, lane, bad);
+        const char LDS_AS* sb = lds + (k % NS) * kStageBytes;
+        f32x16 sacc;
+        stage_scores(sb, sacc);
+        const float mx = stage_max(sacc, t0 + k * kSub);
+        m_seen = fmaxf(m_seen, mx);
+        if (m_run == -INFINITY) m_run = mx;   // first stage of the first pass
+        over |= mx > m_run + kRefHeadroom;
+        stage_pv(sb, sacc);
+      }
+      // All waves are done reading the ring before it is refilled.
+      block_barrier();
+      if (!__syncthreads_or(over)) break;
+      // Redo the item from its first stage with the larger reference.
+      m_run = m_seen;
+      l_run = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p)
+        if (p < nst) issue_stage<NW>(a, lds + p * kStageBytes, b, t0 + p * kSub, t1, w, lane, bad);
+    }
+    pv_drain(o);
+    // ---- finalize ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.0f / l_tot;
+    const float lse_nat = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    if (head_ok) {
+      if (slot < 0) {
+        __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = (__bf16)(o[cb][4 * g + r] * inv);
+            *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = v4;
+          }
+        if (hi == 0) a.lse[size_t(b) * a.H + head] = lse_nat;
+      } else {
+        float* op = a.part_o + (size_t(slot) * a.H + head) * kDV + 4 * hi;
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * inv;
+            *reinterpret_cast<f32x4*>(op + 32 * cb + 8 * g) = v4;
+          }
+        if (hi == 0) a.part_lse[size_t(slot) * a.H + head] = lse_nat;
+      }
+    }
+    if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 256;
+constexpr int kPlanLens = 4096;  // seq_lens staged in LDS per pass
+
+__device__ __forceinline__ int plan_candidate(int i) {
+  // chunk = 32 * k: k = 1..128, then geometric up to 32 * 32768 tokens
+  if (i < 128) return 32 * (i + 1);
+  const int e = i - 128;  // 0..127
+  const float k = 128.0f * exp2f((e + 1) * (8.0f / 128.0f));
+  return 32 * int(k);
+}
+
+// Inclusive block-wide scan of one int per thread; returns (inclusive, total).
+__device__ __forceinline__ int2 block_scan(int v, int* s_scan) {
+  const int tid = threadIdx.x;
+  s_scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int u = (tid >= off) ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += u;
+    __syncthreads();
+  }
+  const int2 r = make_int2(s_scan[tid], s_scan[kPlanThreads - 1]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
+    const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
+    int ovh, int cap, int32_t* __restrict__ hdr, int4* __restrict__ req, int4* __restrict__ items) {
+  __shared__ long long s_cost[kPlanThreads];
+  __shared__ int s_chunk[kPlanThreads];
+  __shared__ int s_scan[kPlanThreads];
+  __shared__ int s_len[kPlanLens];
+  const int tid = threadIdx.x;
+  const int Lmax = M << lgBS;
+
+  // 1) chunk size: each thread prices one candidate,
+  //    cost = ceil(items / slots) * (chunk + per-item overhead).
+  int chunk = forced;
+  if (forced <= 0) {
+    const int T = plan_candidate(tid);
+    long long n = 0;
+    for (int b0 = 0; b0 < B; b0 += kPlanLens) {
+      const int nb = min(kPlanLens, B - b0);
+      for (int i = tid; i < nb; i += kPlanThreads) s_len[i] = min(max(seq_lens[b0 + i], 0), Lmax);
+      __syncthreads();
+      for (int i = 0; i < nb; ++i) n += (s_len[i] + T - 1) / T;
+      __syncthreads();
+    }
+    s_cost[tid] = (n <= cap) ? ((n + n_slots - 1) / n_slots) * (long long)(T + ovh) : (1ll << 62);
+    s_chunk[tid] = T;
+    __syncthreads();
+    for (int st = kPlanThreads / 2; st > 0; st >>= 1) {
+      if (tid < st) {
+        const long long c2 = s_cost[tid + st];
+        const int k2 = s_chunk[tid + st];
+        if (c2 < s_cost[tid] || (c2 == s_cost[tid] && k2 > s_chunk[tid])) {
+          s_cost[tid] = c2;
+          s_chunk[tid] = k2;
+        }
+      }
+      __syncthreads();
+    }
+    chunk = s_chunk[0];
+    // no candidate fits the workspace: one item per request
+    if (s_cost[0] >= (1ll << 62)) chunk = ((Lmax + 31) / 32) * 32;
+    __syncthreads();
+  }
+
+  // 2) totals: full chunks go first, remainders after them
+  int nf_loc = 0, nr_loc = 0, bad = 0;
+  for (int b = tid; b < B; b += kPlanThreads) {
+    const int L0 = seq_lens[b];
+    if (L0 < 0 || L0 > Lmax) bad = 1;
+    const int L = min(max(L0, 0), Lmax);
+    nf_loc += L / chunk;
+    nr_loc += (L % chunk) ? 1 : 0;
+  }
+  const int NF = block_scan(nf_loc, s_scan).y;
+  const int NR = block_scan(nr_loc, s_scan).y;
+  const int any_bad = block_scan(bad, s_scan).y;
+
+  // 3) per-request placement from exclusive scans of (full count, remainder)
+  int carry_f = 0, carry_r = 0;
+  for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
+    const int b = b0 + tid;
+    const int L = (b < B) ? min(max(seq_lens[b], 0), Lmax) : 0;
+    const int nf = L / chunk;
+    const int nr = (L % chunk) ? 1 : 0;
+    const int2 fs = block_scan(nf, s_scan);
+    const int2 rs = block_scan(nr, s_scan);
+    if (b < B) {
+      const int fbeg = carry_f + fs.x - nf;
+      const int cnt = nf + nr;
+      const int ritem = nr ? (NF + carry_r + rs.x - nr) : -1;
+      req[b] = make_int4(fbeg, nf, ritem, cnt);
+      for (int s = 0; s < nf; ++s) {
+        const int idx = fbeg + s;
+        items[idx] = make_int4(b, s * chunk, (s + 1) * chunk, cnt > 1 ? idx : -1);
+      }
+      if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt > 1 ? ritem : -1);
+    }
+    carry_f += fs.y;
+    carry_r += rs.y;
+  }
+
+  // 4) header
+  if (tid == 0) {
+    hdr[0] = NF + NR;
+    hdr[1] = chunk;
+    hdr[2] = any_bad ? MLA_CHECK_SEQ_LEN_RANGE : 0;
+    hdr[3] = 0;
+    hdr[4] = NF;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge
+// ---------------------------------------------------------------------------
+constexpr int kMergeHeads = 8;  // heads per workgroup, 32 threads per head
+
+__global__ __launch_bounds__(256) void mla_merge_kernel(
+    __bf16* __restrict__ out, float* __restrict__ lse, int H,
+    const int4* __restrict__ req, const float* __restrict__ part_lse,
+    const float* __restrict__ part_o) {
+  const int b = blockIdx.x;
+  const int4 r = req[b];
+  const int cnt = r.w;
+  if (cnt == 1) return;
+  const int h = blockIdx.y * kMergeHeads + (threadIdx.x >> 5);
+  if (h >= H) return;
+  const int c0 = (threadIdx.x & 31) * 16;  // 16 columns per thread
+  __bf16* op = out + (size_t(b) * H + h) * kDV + c0;
+  if (cnt == 0) {
+    bf16x8 z = {};
+    *reinterpret_cast<bf16x8*>(op) = z;
+    *reinterpret_cast<bf16x8*>(op + 8) = z;
+    if ((threadIdx.x & 31) == 0) lse[size_t(b) * H + h] = -INFINITY;
+    return;
+  }
+  // items of this request: r.x .. r.x + r.y - 1, then r.z if >= 0
+  float m = -INFINITY;
+  for (int s = 0; s < cnt; ++s) {
+    const int slot = (s < r.y) ? r.x + s : r.z;
+    m = fmaxf(m, part_lse[size_t(slot) * H + h]);
+  }
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+  float lam = 0.0f;
+  for (int s = 0; s < cnt; ++s) {
+    const int slot = (s < r.y) ? r.x + s : r.z;
+    const float wgt = expf(part_lse[size_t(slot) * H + h] - m);
+    lam += wgt;
+    const f32x4* src = reinterpret_cast<const f32x4*>(part_o + (size_t(slot) * H + h) * kDV + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v = src[j];
+      acc[4 * j + 0] += wgt * v[0];
+      acc[4 * j + 1] += wgt * v[1];
+      acc[4 * j + 2] += wgt * v[2];
+      acc[4 * j + 3] += wgt * v[3];
+    }
+  }
+  const float inv = 1.0f / lam;
+  bf16x8 v0, v1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v0[j] = (__bf16)(acc[j] * inv);
+    v1[j] = (__bf16)(acc[8 + j] * inv);
+  }
+  *reinterpret_cast<bf16x8*>(op) = v0;
+  *reinterpret_cast<bf16x8*>(op + 8) = v1;
+  if ((threadIdx.x & 31) == 0) lse[size_t(b) * H + h] = m + logf(lam);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+mla_status device_cu_count(int* n) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  int c = g_cu_count[dev];
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return MLA_ERR_HIP;
+    g_cu_count[dev] = c;
+  }
+  *n = c;
+  return MLA_OK;
+}
+
+int ilog2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+mla_status check_sizes(int32_t B, int32_t H, int32_t M, int32_t BS) {
+  if (B < 0 || H < 0 || M < 0 || BS < 0) return MLA_ERR_BAD_SHAPE;
+  if (H < 1 || H > 128) return MLA_ERR_UNSUPPORTED;
+  const int lg = ilog2_exact(BS);
+  if (lg < 4 || lg > 10) return MLA_ERR_UNSUPPORTED;
+  if (M < 1) return MLA_ERR_BAD_SHAPE;
+  if ((long long)M * BS > (1ll << 28)) return MLA_ERR_BAD_SHAPE;
+  if (B > (1 << 24)) return MLA_ERR_BAD_SHAPE;
+  return MLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mla_status check_workspace(const void* ws, size_t ws_bytes, int B, int H) {
+  if (!ws) return MLA_ERR_NULL_POINTER;
+  if (!aligned(ws, 256)) return MLA_ERR_ALIGNMENT;
+  if (ws_bytes < ws_layout(B, H).total) return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
+
+// Kernel variant for H heads: waves per workgroup and LDS stages.
+struct Variant {
+  int nw, ns, wgs_per_cu;
+};
+Variant pick_variant(int H) {
+  if (H > 64) return {4, 4, 1};
+  if (H > 32) return {2, 2, 2};
+  return {1, 2, 2};
+}
+
+int item_overhead_tokens(int H) { return 32 + 2 * H; }
+
+template <int NW, int NS>
+hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((mla_attend_kernel<NW, NS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS) {
+  if (check_sizes(B, H, M, BS) != MLA_OK) return 0;
+  return ws_layout(B, H).total;
+}
+
+mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t M,
+                           int32_t BS, int32_t chunk_tokens, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (B == 0) return MLA_OK;
+  if (!seq_lens) return MLA_ERR_NULL_POINTER;
+  if (!aligned(seq_lens, 4)) return MLA_ERR_ALIGNMENT;
+  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  const WsLayout L = ws_layout(B, H);
+  if (chunk_tokens < 0) return MLA_ERR_UNSUPPORTED;
+  if (chunk_tokens > 0) {
+    if (chunk_tokens % kSub) return MLA_ERR_UNSUPPORTED;
+    const long long per = ((long long)M * BS + chunk_tokens - 1) / chunk_tokens;
+    if ((long long)B * per > L.cap) return MLA_ERR_UNSUPPORTED;
+  }
+  int ncu = 0;
+  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  const Variant v = pick_variant(H);
+  char* ws = static_cast<char*>(workspace);
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
+                     seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.wgs_per_cu,
+                     (int)chunk_tokens, item_overhead_tokens(H), L.cap,
+                     reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
+                     reinterpret_cast<int4*>(ws + L.item_off));
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_attend(const void* q, const void* latent_cache,
+                             const int32_t* block_table, float scale, void* out, float* lse,
+                             int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (NB < 1) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !latent_cache || !block_table || !out || !lse) return MLA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4))
+    return MLA_ERR_ALIGNMENT;
+  if (!isfinite(scale)) return MLA_ERR_BAD_SCALE;
+  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  int ncu = 0;
+  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  const WsLayout L = ws_layout(B, H);
+  char* ws = static_cast<char*>(workspace);
+  AttendArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.cache = static_cast<const __bf16*>(latent_cache);
+  a.table = block_table;
+  a.out = static_cast<__bf16*>(out);
+  a.lse = lse;
+  a.hdr = reinterpret_cast<int32_t*>(ws);
+  a.items = reinterpret_cast<const int4*>(ws + L.item_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
+  a.part_o = reinterpret_cast<float*>(ws + L.po_off);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.B = B;
+  a.H = H;
+  a.NB = NB;
+  a.M = M;
+  a.lgBS = ilog2_exact(BS);
+  const Variant v = pick_variant(H);
+  const int grid = ncu * v.wgs_per_cu;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  switch (v.nw) {
+    case 4: e = launch_attend<4, 4>(a, grid, st); break;
+    case 2: e = launch_attend<2, 2>(a, grid, st); break;
+    default: e = launch_attend<1, 2>(a, grid, st); break;
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_merge(void* out, float* lse, int32_t B, int32_t H, int32_t M, int32_t BS,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (B == 0) return MLA_OK;
+  if (!out || !lse) return MLA_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_ALIGNMENT;
+  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  const WsLayout L = ws_layout(B, H);
+  char* ws = static_cast<char*>(workspace);
+  dim3 grid(B, (H + kMergeHeads - 1) / kMergeHeads);
+  hipLaunchKernelGGL(mla_merge_kernel, grid, dim3(256), 0, (hipStream_t)stream,
+                     static_cast<__bf16*>(out), lse, (int)H,
+                     reinterpret_cast<const int4*>(ws + L.req_off),
+                     reinterpret_cast<const float*>(ws + L.plse_off),
+                     reinterpret_cast<const float*>(ws + L.po_off));
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode(const void* q, const void* latent_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, float scale, void* out, float* lse, int32_t B,
+                      int32_t H, int32_t NB, int32_t BS, int32_t M, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  // Validate everything up front so that nothing is enqueued on failure.
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (NB < 1) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !latent_cache || !block_table || !seq_lens || !out || !lse)
+    return MLA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_ALIGNMENT;
+  if (!isfinite(scale)) return MLA_ERR_BAD_SCALE;
+  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  if ((s = mla_decode_plan(seq_lens, B, H, M, BS, 0, workspace, workspace_bytes, stream)) != MLA_OK)
+    return s;
+  if ((s = mla_decode_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
+                             workspace, workspace_bytes, stream)) != MLA_OK)
+    return s;
+  return mla_decode_merge(out, lse, B, H, M, BS, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_read_error(const void* workspace, int32_t* flags, void* stream) {
+  if (!workspace || !flags) return MLA_ERR_NULL_POINTER;
+  if (!aligned(workspace, 256)) return MLA_ERR_ALIGNMENT;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return MLA_ERR_HIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, static_cast<const char*>(workspace) + 8, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return MLA_ERR_HIP;
+  *flags = v;
+  return MLA_OK;
+}
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER";
+    case MLA_ERR_BAD_SHAPE: return "MLA_ERR_BAD_SHAPE";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_BAD_SCALE: return "MLA_ERR_BAD_SCALE";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+int32_t mla_decode_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_cache_absorbed_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmla_decode.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert _lib.mla_decode_abi_version() == 1
+    for code, name in [(0, "MLA_OK"), (1, "MLA_ERR_NULL_POINTER"), (2, "MLA_ERR_BAD_SHAPE"),
+                       (3, "MLA_ERR_UNSUPPORTED"), (4, "MLA_ERR_BAD_SCALE"),
+                       (5, "MLA_ERR_WORKSPACE"), (6, "MLA_ERR_HIP"), (7, "MLA_ERR_ALIGNMENT")]:
+        assert _lib.status_string(code) == name
+    assert _lib.status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_workspace_bytes(L):
+    n = _lib.mla_decode_workspace_bytes(124, 128, 64, 64)
+    cap = 124 + 1024
+    assert n >= cap * 128 * 512 * 4 + cap * 128 * 4 + cap * 16 + 124 * 16
+    assert n % 256 == 0
+    assert _lib.mla_decode_workspace_bytes(2, 16, 7, 16) > 0
+    # unsupported sizes give 0
+    assert _lib.mla_decode_workspace_bytes(2, 129, 7, 16) == 0
+    assert _lib.mla_decode_workspace_bytes(2, 0, 7, 16) == 0
+    assert _lib.mla_decode_workspace_bytes(2, 128, 7, 48) == 0
+    assert _lib.mla_decode_workspace_bytes(2, 128, 7, 8) == 0
+    assert _lib.mla_decode_workspace_bytes(2, 128, 0, 16) == 0
+    assert _lib.mla_decode_workspace_bytes(-1, 128, 7, 16) == 0
+    assert _lib.mla_decode_workspace_bytes(1, 128, 1 << 24, 64) == 0  # M*BS > 2^28
+
+
+FAKE = 1 << 20  # a 256-aligned non-null address; never dereferenced on these paths
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, cache=FAKE, table=FAKE, lens=FAKE, scale=0.07, out=FAKE, lse=FAKE,
+             B=2, H=128, NB=14, BS=16, M=7, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return _lib.mla_decode(a["q"], a["cache"], a["table"], a["lens"], a["scale"], a["out"],
+                           a["lse"], a["B"], a["H"], a["NB"], a["BS"], a["M"], a["ws"],
+                           a["wsb"], a["stream"])
+
+
+def test_decode_rejects_bad_arguments_on_host(L):
+    assert _decode(B=0) == _lib.MLA_OK                     # empty batch: nothing to do
+    assert _decode(q=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(cache=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(table=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(lens=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(out=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(lse=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(ws=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode(H=0) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(H=129) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(BS=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(BS=2048) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode(B=-1) == _lib.MLA_ERR_BAD_SHAPE
+    assert _decode(M=0) == _lib.MLA_ERR_BAD_SHAPE
+    assert _decode(NB=0) == _lib.MLA_ERR_BAD_SHAPE
+    assert _decode(scale=float("nan")) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode(scale=float("inf")) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode(wsb=16) == _lib.MLA_ERR_WORKSPACE
+    assert _decode(q=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    assert _decode(cache=FAKE + 4) == _lib.MLA_ERR_ALIGNMENT
+    assert _decode(out=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    assert _decode(lse=FAKE + 2) == _lib.MLA_ERR_ALIGNMENT
+    assert _decode(ws=FAKE + 128) == _lib.MLA_ERR_ALIGNMENT
+
+
+def test_plan_attend_merge_reject_bad_arguments_on_host(L):
+    P = _lib.mla_decode_plan
+    assert P(FAKE, 0, 128, 7, 16, 0, FAKE, 1 << 40, None) == _lib.MLA_OK
+    assert P(None, 2, 128, 7, 16, 0, FAKE, 1 << 40, None) == _lib.MLA_ERR_NULL_POINTER
+    assert P(FAKE, 2, 128, 7, 16, 0, None, 1 << 40, None) == _lib.MLA_ERR_NULL_POINTER
+    assert P(FAKE, 2, 128, 7, 16, 0, FAKE, 8, None) == _lib.MLA_ERR_WORKSPACE
+    assert P(FAKE, 2, 128, 7, 16, 48, FAKE, 1 << 40, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert P(FAKE, 2, 128, 7, 16, -32, FAKE, 1 << 40, None) == _lib.MLA_ERR_UNSUPPORTED
+    # forced chunk that would need more work items than the workspace holds
+    assert P(FAKE, 100, 128, 4096, 64, 32, FAKE, 1 << 40, None) == _lib.MLA_ERR_UNSUPPORTED
+    A = _lib.mla_decode_attend
+    assert A(None, FAKE, FAKE, 0.1, FAKE, FAKE, 2, 128, 14, 16, 7, FAKE, 1 << 40, None) \
+        == _lib.MLA_ERR_NULL_POINTER
+    assert A(FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, 2, 128, 14, 16, 7, FAKE, 1 << 40,
+             None) == _lib.MLA_ERR_BAD_SCALE
+    assert A(FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 2, 128, 0, 16, 7, FAKE, 1 << 40, None) \
+        == _lib.MLA_ERR_BAD_SHAPE
+    Mg = _lib.mla_decode_merge
+    assert Mg(None, FAKE, 2, 128, 7, 16, FAKE, 1 << 40, None) == _lib.MLA_ERR_NULL_POINTER
+    assert Mg(FAKE, FAKE, 2, 128, 7, 16, FAKE, 4, None) == _lib.MLA_ERR_WORKSPACE
+    assert _lib.lib().mla_decode_read_error(None, ctypes.byref(ctypes.c_int32()), None) \
+        == _lib.MLA_ERR_NULL_POINTER
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
