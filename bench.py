@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of absorbed-MLA decode on one MI355X.
+
+One step = one whole decode call (plan + attend) of one layer over the
+DP-attention-rank workload: 124 requests x 4,096 cached tokens, 128 heads,
+576-wide bf16 latent in 64-token pages with a shuffled block table.  Inputs
+are resident in HBM before the timed region; three independent caches are
+rotated so that no timed call finds its cache in the 256 MB Infinity Cache.
+
+Prints one JSON line with the metric (cached-token reads/s), a roofline
+record for the attend kernel (HIP events around every attend launch on the
+stream it runs on), and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dp_rank]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MLA decode: cached-token reads/s, achieved HBM TB/s, % of roofline"
+COUNTERS = os.path.join(ROOT, "profiles", "attend_dp_rank_hbm_counters.json")
+SRC = os.path.join(ROOT, "mla_latent_cache_absorbed_amd", "csrc", "mla_decode.hip")
+
+
+def src_hash() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dp_rank",
+                   choices=["dp_rank", "tp_slice", "ragged", "step61"])
+    p.add_argument("--copies", type=int, default=3, help="independent caches rotated")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run only a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def hbm_traffic_record():
+    """Counter-measured HBM bytes per attend launch, if taken on this source."""
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if rec.get("src_sha256_16") != src_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle, as it stands, on whole requests of the workload until the budget."""
+    import numpy as np
+    from mla_latent_cache_absorbed_amd import workloads as wl
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    lens = w.seq_lens_list()
+    done_tokens = 0
+    done_req = 0
+    elapsed = 0.0
+    for b in range(w.B):
+        L = lens[b]
+        nblk = -(-L // w.BS)
+        sub = wl.bf16_bits(w.cache[w.block_table[b, :nblk].long()])
+        qb = wl.bf16_bits(w.q[b:b + 1])
+        t0 = time.perf_counter()
+        orc.oracle_decode(qb, sub, np.arange(nblk, dtype=np.int32)[None],
+                          np.array([L], dtype=np.int32), w.scale)
+        elapsed += time.perf_counter() - t0
+        done_tokens += L
+        done_req += 1
+        if elapsed >= budget_s:
+            break
+    return {"value": done_tokens / elapsed, "unit": "cached-token reads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done_req} of {w.B} requests ({done_tokens} tokens x {w.H} heads), "
+                      f"float64 NumPy, {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
+              "path has no multi-GPU code", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_probe:
+        copy_probe()
+        return
+    import mla_latent_cache_absorbed_amd as mla
+    from mla_latent_cache_absorbed_amd import accounting as acc
+    from mla_latent_cache_absorbed_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    name = args.workload
+    spec = wl.spec(name)
+    layers = spec.layers
+    ncopies = layers if name == "step61" else max(1, args.copies)
+    print(f"[bench] generating {ncopies} x {name} on {torch.cuda.get_device_name(0)}",
+          file=sys.stderr, flush=True)
+    ws_list = []
+    wls = []
+    for i in range(ncopies):
+        w = wl.make(name, device=dev, seed=0, layer=i) if name == "step61" else \
+            wl.make(name, device=dev, seed=0) if i == 0 else None
+        if w is None:  # extra copies: same table and lengths, fresh q and cache
+            base = wls[0]
+            g = torch.Generator(device=dev).manual_seed(1000 + i)
+            q = torch.randn(base.q.shape, generator=g, device=dev).to(torch.bfloat16)
+            c = torch.randn(base.cache.shape, generator=g, device=dev).to(torch.bfloat16)
+            w = wl.Workload(name, q, c, base.block_table, base.seq_lens, base.scale)
+        wls.append(w)
+    w0 = wls[0]
+    B, H, M, BS, NB = w0.B, w0.H, w0.M, w0.BS, w0.NB
+    ws = mla.Workspace(B, H, M, BS, dev)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    seq = w0.seq_lens_list()
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        # one decode step: plan, then one attend per layer
+        mla.plan(w0.seq_lens, H, M, BS, ws)
+        for l in range(layers):
+            w = wls[(i * layers + l) % len(wls)]
+            if ev is not None:
+                ev[0].record()
+            mla.attend(w.q, w.cache, w.block_table, w.scale, out, lse, ws)
+            if ev is not None:
+                ev[1].record()
+                ev.pop(0)
+                ev.pop(0)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n_attend = args.steps * layers
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_attend)]
+    pairs = [(evs[2 * j], evs[2 * j + 1]) for j in range(n_attend)]
+    queue = [e for p in pairs for e in p]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, queue)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    attend_ms = [a.elapsed_time(b) for a, b in pairs]
+    attend_avg_ms = sum(attend_ms) / len(attend_ms)
+    hdr = ws.header()
+
+    tokens_step = acc.token_reads(seq, layers)
+    value = tokens_step / (ms_step * 1e-3)
+    alg_bytes = acc.algorithmic_bytes(seq, H, BS)         # per attend launch (one layer)
+    alg_flops = acc.algorithmic_flops(seq, H)
+    achieved_gbs = alg_bytes / (attend_avg_ms * 1e-3) / 1e9
+    tflops = alg_flops / (attend_avg_ms * 1e-3) / 1e12
+    step_gbs = layers * alg_bytes / (ms_step * 1e-3) / 1e9
+    intensity = alg_flops / alg_bytes
+    bound = "hbm" if intensity < MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    roof_t = max(alg_bytes / (HBM_PEAK_GBS * 1e9), alg_flops / (MFMA_BF16_PEAK_TFS * 1e12))
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "cached-token reads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "seq_lens": "4096 each" if name in
+                   ("dp_rank", "tp_slice", "step61") else f"sum {sum(seq)}",
+                   "heads": H, "block_size": BS, "blocks": NB, "layers": layers,
+                   "cache_copies": len(wls)},
+        "achieved_hbm_tb_s": step_gbs / 1e3,
+        "roofline_frac_step": roof_t * layers / (ms_step * 1e-3),
+        "roofline": {
+            "bound": bound,
+            "kernel": "mla_attend_kernel",
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": hbm_traffic_record(),
+            "launch_ms": attend_avg_ms,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": tflops,
+            "mfma_frac": tflops / MFMA_BF16_PEAK_TFS,
+            "intensity_flop_per_byte": intensity,
+        },
+        "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -76,12 +76,13 @@ typedef enum {
 
 /* Bytes of workspace needed for a batch of B requests with H heads, a block
  * table of M entries per request and block size BS.  Returns 0 when the sizes
- * are outside the supported set.  The figure covers the work plan and fp32
- * split-KV partials for at most B + 1024 work items. */
+ * are outside the supported set.  The figure covers the work plan, one
+ * arrival counter per request and fp32 split-KV partials for at most
+ * B + 1024 work items. */
 size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS);
 
-/* Whole decode: plan, attend, merge — the three calls below in order.  The
- * chunk size of the split-KV plan is chosen on the device from seq_lens. */
+/* Whole decode: the plan call followed by the attend call below.  The chunk
+ * size of the split-KV plan is chosen on the device from seq_lens. */
 mla_status mla_decode(const void* q, const void* latent_cache,
                       const int32_t* block_table, const int32_t* seq_lens,
                       float scale, void* out, float* lse,
@@ -90,42 +91,38 @@ mla_status mla_decode(const void* q, const void* latent_cache,
 
 /* Step 1 — split-KV work plan.  One small kernel reads seq_lens and writes
  * into the workspace a list of work items (request, token range), each at
- * most chunk_tokens long, ordered full chunks first.  chunk_tokens = 0 lets
- * the device pick the chunk (a multiple of 32 tokens) that minimises an
- * estimate of the makespan on this GPU's compute units; a positive value
- * forces that chunk size (it must be a multiple of 32, and
- * B * ceil(M*BS / chunk_tokens) must not exceed B + 1024).  The plan depends
- * only on seq_lens, so one plan serves every layer of a decode step.
+ * most chunk_tokens long: full chunks first, then each request's shorter last
+ * chunk, then one item per empty request.  chunk_tokens = 0 lets the device
+ * pick the chunk (a multiple of 32 tokens) that minimises an estimate of the
+ * makespan on this GPU's compute units; a positive value forces that chunk
+ * size (it must be a multiple of 32, and B * ceil(M*BS / chunk_tokens) must
+ * not exceed B + 1024).  The plan depends only on seq_lens, so one plan
+ * serves every layer of a decode step.
  *
  * Workspace layout written by the plan (int32 words unless noted):
  *   [0] number of work items   [1] chunk tokens   [2] data-check bits
  *   [3] work-queue counter (0 after the plan and after every attend call)
  *   [4] number of full items
  *   at byte 256: per request 4 words (first full item, full-item count,
- *   remainder item or -1, total item count);
- *   then per item 4 words (request, first token, end token, partial slot or
- *   -1 when the item writes out/lse directly). */
+ *   remainder item or -1, total item count); then, 256-byte aligned, one
+ *   arrival counter per request (0 between calls); then per item 4 words
+ *   (request, first token, end token, the request's item count). */
 mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
                            int32_t M, int32_t BS, int32_t chunk_tokens,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Step 2 — attention over each work item (the hot kernel).  For an item that
- * covers a whole request it writes out/lse; otherwise it writes the item's
- * normalised fp32 output and its log-sum-exp as a partial result into the
- * workspace.  Needs a plan made with the same B, H, M, BS. */
+/* Step 2 — attention over every work item of the plan (the hot kernel), and
+ * the split-KV merge.  An item that covers a whole request writes out/lse
+ * directly; an empty request gets out = 0, lse = -inf.  When a request is
+ * split, each of its items writes its normalised fp32 output and log-sum-exp
+ * into the workspace, and the last of them to finish merges all of them:
+ * lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s (bf16, RNE).
+ * Needs a plan made with the same B, H, M, BS. */
 mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              const int32_t* block_table, float scale,
                              void* out, float* lse,
                              int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
                              void* workspace, size_t workspace_bytes, void* stream);
-
-/* Step 3 — log-sum-exp merge of the partial results of every split request:
- * lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s (bf16, RNE).
- * Requests with no tokens get out = 0, lse = -inf.  Requests that were not
- * split are left as step 2 wrote them. */
-mla_status mla_decode_merge(void* out, float* lse, int32_t B, int32_t H,
-                            int32_t M, int32_t BS,
-                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream`, then copies the data-check word of the workspace
  * into *flags (0 = no violation seen since the last plan). */

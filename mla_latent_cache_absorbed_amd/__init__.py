@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import MlaError  # noqa: F401
 
-__all__ = ["decode", "Workspace", "plan", "attend", "merge", "MlaError"]
+__all__ = ["decode", "Workspace", "plan", "attend", "MlaError"]
 
 
 def _stream() -> int:
@@ -78,7 +78,7 @@ def decode(q: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tenso
            seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
            lse: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None
            ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Absorbed MLA decode of one layer (plan + attend + merge)."""
+    """Absorbed MLA decode of one layer (plan + attend)."""
     _check_inputs(q, latent_cache, block_table, seq_lens)
     B, H, _ = q.shape
     NB, BS, _ = latent_cache.shape
@@ -111,10 +111,3 @@ def attend(q, latent_cache, block_table, scale, out, lse, workspace: Workspace) 
                                 float(scale), out.data_ptr(), lse.data_ptr(), B, H, NB, BS, M,
                                 workspace.ptr, workspace.nbytes, _stream())
     _lib._check("mla_decode_attend", st)
-
-
-def merge(out, lse, M: int, BS: int, workspace: Workspace) -> None:
-    B, H, _ = out.shape
-    st = _lib.mla_decode_merge(out.data_ptr(), lse.data_ptr(), B, H, M, BS, workspace.ptr,
-                               workspace.nbytes, _stream())
-    _lib._check("mla_decode_merge", st)

@@ -35,7 +35,6 @@ SIGNATURES = {
     "mla_decode": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_decode_plan": (_I, [_P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_decode_attend": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
-    "mla_decode_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "mla_decode_read_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_decode_abi_version": (_I, []),
@@ -98,10 +97,6 @@ def mla_decode_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, B
                       workspace, workspace_bytes, stream) -> int:
     return lib().mla_decode_attend(q, latent_cache, block_table, scale, out, lse,
                                    B, H, NB, BS, M, workspace, workspace_bytes, stream)
-
-
-def mla_decode_merge(out, lse, B, H, M, BS, workspace, workspace_bytes, stream) -> int:
-    return lib().mla_decode_merge(out, lse, B, H, M, BS, workspace, workspace_bytes, stream)
 
 
 def mla_decode_read_error(workspace, stream) -> int:

@@ -1,6 +1,6 @@
 // Absorbed-MLA decode over a paged 576-wide bf16 latent cache, for gfx950.
 //
-// Three kernels behind the C ABI declared in include/mla_decode.h:
+// Two kernels behind the C ABI declared in include/mla_decode.h:
 //
 //   mla_plan_kernel    one workgroup: reads seq_lens, picks a split-KV chunk
 //                      size, writes the list of (request, token range) work
@@ -13,10 +13,12 @@
 //                      S^T[token, head] = K * Q^T over all 576 dims and the
 //                      weighted sum O^T[col, head] += V^T * P^T over the 512
 //                      kv_c dims run on 32x32x16 bf16 MFMA with fp32
-//                      accumulation; the softmax is an fp32 online softmax in
-//                      the exp2 domain with a lazily moved running max.
-//   mla_merge_kernel   log-sum-exp merge of the partial results of split
-//                      requests.
+//                      accumulation, software-pipelined: the score MFMAs of
+//                      stage k+1 are interleaved with the weighted-sum MFMAs
+//                      of stage k.  When a request is split over several
+//                      items, each writes a normalised fp32 partial and its
+//                      log-sum-exp, and the last item of the request to
+//                      finish merges them (split-KV log-sum-exp merge).
 //
 // The operation: each head's absorbed query attends over the shared latent
 // directly (page "DP attention + expert parallel: MLA KV replication",
@@ -45,16 +47,20 @@ constexpr int kLoadsPerStage = kSub + 4;  // 1 KB direct-to-LDS loads per stage
 constexpr int kMaxExtraItems = 1024;      // work items beyond B the workspace holds
 constexpr int kHdrBytes = 256;
 constexpr float kRefHeadroom = 64.0f;     // log2 units: P <= 2^64 before an item is redone
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kSc1 = 16;                  // cache-policy bit: agent-coherent access
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
 
 // Workspace sections (byte offsets).
 struct WsLayout {
-  size_t req_off, item_off, plse_off, po_off, total;
+  size_t req_off, ctr_off, item_off, plse_off, po_off, total;
   int cap;
 };
 
@@ -64,7 +70,8 @@ __host__ __device__ inline WsLayout ws_layout(int B, int H) {
   WsLayout w;
   w.cap = B + kMaxExtraItems;
   w.req_off = kHdrBytes;
-  w.item_off = align256(w.req_off + size_t(B) * 16);
+  w.ctr_off = align256(w.req_off + size_t(B) * 16);
+  w.item_off = align256(w.ctr_off + size_t(B) * 4);
   w.plse_off = align256(w.item_off + size_t(w.cap) * 16);
   w.po_off = align256(w.plse_off + size_t(w.cap) * H * 4);
   w.total = align256(w.po_off + size_t(w.cap) * H * kDV * 4);
@@ -113,7 +120,7 @@ __device__ __forceinline__ void block_barrier() {
 // and then spills.  Hazards the compiler cannot see through inline asm are
 // covered here: every MFMA is preceded by two wait states (a VALU write of an
 // operand just before it); back-to-back accumulation into the same
-// registers needs none; mfma_drain() provides >= 19 wait states between the
+// registers needs none; the drains provide >= 19 wait states between the
 // last XDL write of an accumulator and any non-MFMA access to it.
 __device__ __forceinline__ void qk_mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
@@ -141,9 +148,11 @@ struct AttendArgs {
   __bf16* out;
   float* lse;
   int32_t* hdr;          // workspace header (n_items, chunk, check bits, queue)
-  const int4* items;     // work items
-  float* part_lse;       // [cap, H]
-  float* part_o;         // [cap, H, 512]
+  const int4* req;       // per request: first full item, full count, remainder item, count
+  int32_t* ctr;          // per request: arrivals of split items (0 between calls)
+  const int4* items;     // per item: request, first token, end token, request's item count
+  float* part_lse;       // [cap, H]  log2-domain log-sum-exp of each split item
+  float* part_o;         // [cap, H, 512] normalised output of each split item
   float scale_log2;      // scale * log2(e)
   int32_t B, H, NB, M, lgBS;
 };
@@ -155,6 +164,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* cache, 
                                            (int)blk_bytes, 0x00020000);
 }
 
+// Direct-to-LDS loads, written out: the LDS address goes in M0 and each lane's
+// 16 bytes land at M0 + 16 * lane.  The compiler does not model these as LDS
+// writes, so it adds no waits of its own before later LDS reads; the stage
+// pipeline waits for them explicitly (vmcnt counts them in issue order).
+// One wait state after the M0 write precedes each load.
+__device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                             const char LDS_AS* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma16_global(const char* src, const char LDS_AS* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "{m0}"(m0) : "memory");
+}
+
 // Issue this wave's share of the direct-to-LDS loads of one stage (32/NW
 // region-A rows and 4/NW region-B loads).  Tokens past `t1` are clamped to
 // t1-1, a row of the request that is always valid; the softmax masks them.
@@ -164,7 +190,8 @@ __device__ __forceinline__ void issue_stage(const AttendArgs& a, char LDS_AS* sb
   const int lg = a.lgBS;
   const int bs_mask = (1 << lg) - 1;
   const uint32_t blk_bytes = uint32_t(kD * 2) << lg;
-  const int32_t* trow = a.table + size_t(b) * a.M;
+  // uniform reads of a table that is constant during the kernel: scalar loads
+  const CONST_AS int32_t* trow = (const CONST_AS int32_t*)(a.table) + size_t(b) * a.M;
   const int last = t1 - 1;
   // base is a multiple of 32 and BS >= 16: at most two blocks per stage
   const int lb0 = base >> lg;
@@ -176,45 +203,56 @@ __device__ __forceinline__ void issue_stage(const AttendArgs& a, char LDS_AS* sb
   const char* cbase = reinterpret_cast<const char*>(a.cache);
   const __amdgpu_buffer_rsrc_t r0 = block_rsrc(cbase, blk0, blk_bytes);
   const __amdgpu_buffer_rsrc_t r1 = block_rsrc(cbase, blk1, blk_bytes);
-  const uint32_t lane16 = uint32_t(lane) * 16;
+  uint32_t lane16 = uint32_t(lane) * 16;
+  // Keep the per-lane load offsets from being hoisted out of the item loop
+  // (they would be spilled and reloaded with a full vmcnt wait).
+  asm volatile("" : "+v"(lane16));
 #pragma unroll
   for (int k = 0; k < kSub / NW; ++k) {
     const int i = w + NW * k;                 // region-A row, wave-uniform
     const int tok = min(base + i, last);
     const uint32_t voff = uint32_t(tok & bs_mask) * (kD * 2) + (lane16 ^ uint32_t(swzA(i) * 16));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(((tok >> lg) == lb0) ? r0 : r1, sbuf + i * 1024, 16,
-                                             voff, 0, 0, 0);
+    dma16_buffer(((tok >> lg) == lb0) ? r0 : r1, voff, sbuf + i * 1024);
   }
 #pragma unroll
   for (int k = 0; k < 4 / NW; ++k) {
     const int j = w + NW * k;                 // region-B load: chunks 2j, 2j+1
-    const int t = lane & 31;
-    const int cp = 2 * j + (lane >> 5);
+    const int t = (lane16 >> 4) & 31;
+    const int cp = 2 * j + (lane16 >> 9);
     const int tok = min(base + t, last);
     const int blk = ((tok >> lg) == lb0) ? blk0 : blk1;
     const size_t row = (size_t(blk) << lg) | size_t(tok & bs_mask);
     const char* src = cbase + row * (kD * 2) + 1024 + cp * 16;
-    __builtin_amdgcn_global_load_lds(src, sbuf + kRegionB + j * 1024, 16, 0, 0);
+    dma16_global(src, sbuf + kRegionB + j * 1024);
   }
 }
 
 template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
+  static_assert(NS >= 3, "the pipeline reads two stages while one more loads");
   __shared__ __attribute__((aligned(1024))) char lds_raw[NS * kStageBytes];
   __shared__ int s_item;
+  __shared__ int s_ticket;
   char LDS_AS* lds = (char LDS_AS*)(lds_raw);
 
   constexpr int LPW = kLoadsPerStage / NW;  // loads per wave per stage
-  constexpr int PFK = 4;                    // QK operand reads in flight
-  constexpr int PFV = 4;                    // PV operand reads in flight
+  constexpr int PF = 3;                     // operand reads in flight per MFMA stream
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int hl = lane & 31;
   const int hi = lane >> 5;
   const int head = w * 32 + hl;
   const bool head_ok = head < a.H;
-  const int n_items = __builtin_amdgcn_readfirstlane(a.hdr[0]);
+  const int n_items = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[0]);
+  // lanes l and l^32 hold the same head: exchange through ds_bpermute
+  const int xlane = (lane ^ 32) << 2;
+  auto pair_max = [&](float x) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_ds_bpermute(xlane, __float_as_int(x))));
+  };
+  auto pair_sum = [&](float x) {
+    return x + __int_as_float(__builtin_amdgcn_ds_bpermute(xlane, __float_as_int(x)));
+  };
 
   // Per-lane LDS offsets of the MFMA operand reads (relative to a stage).
   // QK region A: k-step s = 8q + j reads chunk 2s + hi of token hl at
@@ -255,74 +293,66 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       break;
     }
 
-    const int4 item = a.items[it];
-    const int b = __builtin_amdgcn_readfirstlane(item.x);
-    const int t0 = __builtin_amdgcn_readfirstlane(item.y);
-    const int t1 = __builtin_amdgcn_readfirstlane(item.z);
-    const int slot = __builtin_amdgcn_readfirstlane(item.w);
+    const i32x4 item = ((const CONST_AS i32x4*)a.items)[it];
+    const int b = __builtin_amdgcn_readfirstlane(item[0]);
+    const int t0 = __builtin_amdgcn_readfirstlane(item[1]);
+    const int t1 = __builtin_amdgcn_readfirstlane(item[2]);
+    const int cnt = __builtin_amdgcn_readfirstlane(item[3]);
+
+    if (t1 <= t0) {
+      // a request with no cached tokens: out = 0, lse = -inf
+      if (head_ok) {
+        __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
+        const bf16x4 z = {};
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = z;
+        if (hi == 0) a.lse[size_t(b) * a.H + head] = -INFINITY;
+      }
+      continue;
+    }
     const int nst = (t1 - t0 + kSub - 1) / kSub;
     int bad = 0;
-
-    // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
-    // lane holds head hl, dims 16s + 8hi .. +7.
-    bf16x8 qreg[36];
-    {
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-          a.q + (size_t(b) * a.H + (head_ok ? head : 0)) * kD + 8 * hi);
-#pragma unroll
-      for (int s = 0; s < 36; ++s) {
-        bf16x8 v = qp[2 * s];
-        if (!head_ok) v = bf16x8{};
-        qreg[s] = v;
-      }
-    }
-
-    // Prologue: stages 0 .. NS-2.
-#pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < nst) issue_stage<NW>(a, lds + p * kStageBytes, b, t0 + p * kSub, t1, w, lane, bad);
 
     f32x16 o[16];
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.0f;
+    float m_run = -INFINITY;   // exponent reference of this head (log2 units)
+    float m_seen = -INFINITY;  // largest scaled score seen
+    float l_run = 0.0f;        // this lane's share of the row sum
 
-    // ---- stage pieces ----
-    // Scores S^T[token, head] over all 576 dims; lane holds head hl and
-    // tokens 8(v/4) + 4hi + (v%4) of the stage in sacc[v].
-    auto stage_scores = [&](const char LDS_AS* sb, f32x16& sacc) {
-      bf16x8 kf[PFK];
-#define MLA_KREAD(s)                                                                   \
-  ((s) < 32 ? *(const bf16x8 LDS_AS*)(sb + qk_off[(s) & 7] + 256 * ((s) >> 3))        \
-            : *(const bf16x8 LDS_AS*)(sb + qkb + 1024 * ((s) - 32)))
-#pragma unroll
-      for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(s);
-#pragma unroll
-      for (int s = 0; s < 36; ++s) {
-        if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
-        else qk_mfma(sacc, kf[s % PFK], qreg[s]);
-        if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(s + PFK);
-      }
-#undef MLA_KREAD
-      qk_drain(sacc);
-    };
-    // Scale to the exp2 domain, mask tokens >= t1, return the per-head max.
+#define MLA_KREAD(sb, s)                                                               \
+  ((s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))      \
+            : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
+#define MLA_VREAD(sb, n, dst)                                                               \
+  do {                                                                                      \
+    const int cb_ = (n) & 15, kk_ = (n) >> 4;                                               \
+    const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                        \
+    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
+        (bf16x4 LDS_AS*)((sb) + pv_off[0][cb_ & 3] + imm_));                                \
+    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
+        (bf16x4 LDS_AS*)((sb) + pv_off[1][cb_ & 3] + imm_));                                \
+    dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
+  } while (0)
+
+    // Scale scores to the exp2 domain, mask tokens >= t1; return the per-head
+    // max (lanes l and l^32 hold the same head and combine their halves).
     auto stage_max = [&](f32x16& sacc, int base) -> float {
+      // register v holds token base + 4hi + 8(v/4) + (v%4): valid while
+      // 8(v/4) + (v%4) < t1 - base - 4hi
+      const int lim = t1 - base - 4 * hi;
       float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int tk = base + 8 * (v >> 2) + 4 * hi + (v & 3);
-        const float x = (tk < t1) ? sacc[v] * a.scale_log2 : -INFINITY;
+        const float x = (8 * (v >> 2) + (v & 3) < lim) ? sacc[v] * a.scale_log2 : -INFINITY;
         sacc[v] = x;
         mx = fmaxf(mx, x);
       }
-      return fmaxf(mx, __shfl_xor(mx, 32));  // lanes l and l^32 hold the same head
+      return pair_max(mx);
     };
-    // P = exp2(S - m_run) (bf16 for the MFMA), row sums, and
-    // O^T[col, head] += V^T[col, token] * P^T[token, head].
-    auto stage_pv = [&](const char LDS_AS* sb, const f32x16& sacc) {
-      bf16x8 p0, p1;
+    // P = 2^(S - m_run) as bf16 MFMA operands (tokens 0-15 in p0, 16-31 in p1).
+    auto stage_p = [&](const f32x16& sacc, bf16x8& p0, bf16x8& p1) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float pv = __builtin_amdgcn_exp2f(sacc[v] - m_run);
@@ -330,54 +360,108 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         if (v < 8) p0[v] = (__bf16)pv;
         else p1[v - 8] = (__bf16)pv;
       }
-      // order n = 16 kk + cb: consecutive MFMAs use different accumulators
-      bf16x8 vf[PFV];
-#define MLA_VREAD(n, dst)                                                                   \
-  do {                                                                                      \
-    const int cb_ = (n) & 15, kk_ = (n) >> 4;                                               \
-    const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                        \
-    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)(sb + pv_off[0][cb_ & 3] + imm_));                                  \
-    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)(sb + pv_off[1][cb_ & 3] + imm_));                                  \
-    dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
-  } while (0)
-#pragma unroll
-      for (int n = 0; n < PFV; ++n) MLA_VREAD(n, vf[n]);
-#pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        pv_mfma(o[n & 15], vf[n % PFV], (n >> 4) ? p1 : p0);
-        if (n + PFV < 32) MLA_VREAD(n + PFV, vf[n % PFV]);
-      }
-#undef MLA_VREAD
     };
 
-    // ---- stage loop ----
+    // ---- stage pipeline ----
     // Each head's exponent reference m_run is fixed from the item's first
     // stage (where O is still zero), so O is never rescaled: P = 2^(s - m_run)
     // may grow up to 2^kRefHeadroom on later stages, which fp32 sums and bf16
     // weights carry exactly in relative terms.  If a later score exceeds the
     // reference by more than that (not seen with attention-like data), the
     // whole item is redone with the larger reference.
-    float m_seen = -INFINITY;
+    //
+    // Iteration k holds P(k) and runs the score MFMAs of stage k+1
+    // interleaved with the weighted-sum MFMAs of stage k; stages k+2 ..
+    // k+NS-2 stay in flight.
     for (;;) {
       bool over = false;
-      for (int k = 0; k < nst; ++k) {
-        // Wait for this wave's loads of stage k; later stages may stay in flight.
-        if (k + NS - 2 < nst) wait_vmcnt_lgkm0<LPW * (NS - 2)>();
+      // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
+      // lane holds head hl, dims 16s + 8hi .. +7 (reloaded on a redo so that
+      // they are not live past the last score MFMA of a pass).
+      bf16x8 qreg[36];
+      {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            a.q + (size_t(b) * a.H + (head_ok ? head : 0)) * kD + 8 * hi);
+#pragma unroll
+        for (int s = 0; s < 36; ++s) {
+          bf16x8 v = qp[2 * s];
+          if (!head_ok) v = bf16x8{};
+          qreg[s] = v;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p)
+        if (p < nst) issue_stage<NW>(a, lds + p * kStageBytes, b, t0 + p * kSub, t1, w, lane, bad);
+      // stage 0 scores (a lone chain, once per item)
+      if (nst >= NS - 1) wait_vmcnt_lgkm0<LPW * (NS - 2)>();
+      else if (nst == 2) wait_vmcnt_lgkm0<LPW>();
+      else wait_vmcnt_lgkm0<0>();
+      block_barrier();
+      f32x16 sacc;
+      {
+        const char LDS_AS* sb = lds;
+        bf16x8 kf[PF];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) kf[s] = MLA_KREAD(sb, s);
+#pragma unroll
+        for (int s = 0; s < 36; ++s) {
+          if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
+          else qk_mfma(sacc, kf[s % PF], qreg[s]);
+          if (s + PF < 36) kf[s % PF] = MLA_KREAD(sb, s + PF);
+        }
+        qk_drain(sacc);
+      }
+      bf16x8 p0, p1;
+      {
+        const float mx = stage_max(sacc, t0);
+        m_seen = fmaxf(m_seen, mx);
+        if (m_run == -INFINITY) m_run = mx;
+        over |= mx > m_run + kRefHeadroom;
+        stage_p(sacc, p0, p1);
+      }
+      for (int k = 0; k + 1 < nst; ++k) {
+        const char LDS_AS* sbv = lds + (k % NS) * kStageBytes;
+        // stage k+1 must be in LDS; stage k+2 may still be loading
+        if (k + 2 < nst) wait_vmcnt_lgkm0<LPW * (NS - 3)>();
         else wait_vmcnt_lgkm0<0>();
         block_barrier();
         if (k + NS - 1 < nst)
           issue_stage<NW>(a, lds + ((k + NS - 1) % NS) * kStageBytes, b,
                           t0 + (k + NS - 1) * kSub, t1, w, lane, bad);
-        const char LDS_AS* sb = lds + (k % NS) * kStageBytes;
-        f32x16 sacc;
-        stage_scores(sb, sacc);
-        const float mx = stage_max(sacc, t0 + k * kSub);
+        const char LDS_AS* sbk = lds + ((k + 1) % NS) * kStageBytes;
+        bf16x8 kf[PF], vf[PF];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+          kf[s] = MLA_KREAD(sbk, s);
+          MLA_VREAD(sbv, s, vf[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < 36; ++s) {
+          if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
+          else qk_mfma(sacc, kf[s % PF], qreg[s]);
+          if (s + PF < 36) kf[s % PF] = MLA_KREAD(sbk, s + PF);
+          if (s < 32) {
+            pv_mfma(o[s & 15], vf[s % PF], (s >> 4) ? p1 : p0);
+            if (s + PF < 32) MLA_VREAD(sbv, s + PF, vf[s % PF]);
+          }
+        }
+        qk_drain(sacc);
+        const float mx = stage_max(sacc, t0 + (k + 1) * kSub);
         m_seen = fmaxf(m_seen, mx);
-        if (m_run == -INFINITY) m_run = mx;   // first stage of the first pass
         over |= mx > m_run + kRefHeadroom;
-        stage_pv(sb, sacc);
+        stage_p(sacc, p0, p1);
+      }
+      {
+        // weighted sum of the last stage
+        const char LDS_AS* sbv = lds + ((nst - 1) % NS) * kStageBytes;
+        bf16x8 vf[PF];
+#pragma unroll
+        for (int s = 0; s < PF; ++s) MLA_VREAD(sbv, s, vf[s]);
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+          pv_mfma(o[s & 15], vf[s % PF], (s >> 4) ? p1 : p0);
+          if (s + PF < 32) MLA_VREAD(sbv, s + PF, vf[s % PF]);
+        }
       }
       // All waves are done reading the ring before it is refilled.
       block_barrier();
@@ -385,19 +469,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       // Redo the item from its first stage with the larger reference.
       m_run = m_seen;
       l_run = 0.0f;
+      pv_drain(o);
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
-#pragma unroll
-      for (int p = 0; p < NS - 1; ++p)
-        if (p < nst) issue_stage<NW>(a, lds + p * kStageBytes, b, t0 + p * kSub, t1, w, lane, bad);
     }
+#undef MLA_KREAD
+#undef MLA_VREAD
     pv_drain(o);
+    if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
+
     // ---- finalize ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.0f / l_tot;
-    const float lse_nat = (m_run + log2f(l_tot)) * 0.69314718055994531f;
-    if (head_ok) {
-      if (slot < 0) {
+    const float l_tot = pair_sum(l_run);
+    const float lse2 = m_run + log2f(l_tot);  // log2 of sum_t 2^(scaled score)
+    if (cnt == 1) {
+      if (head_ok) {
+        const float inv = 1.0f / l_tot;
         __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb)
@@ -408,22 +494,94 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
             for (int r = 0; r < 4; ++r) v4[r] = (__bf16)(o[cb][4 * g + r] * inv);
             *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = v4;
           }
-        if (hi == 0) a.lse[size_t(b) * a.H + head] = lse_nat;
-      } else {
-        float* op = a.part_o + (size_t(slot) * a.H + head) * kDV + 4 * hi;
+        if (hi == 0) a.lse[size_t(b) * a.H + head] = lse2 * kLn2;
+      }
+      continue;
+    }
+
+    // Split request: publish this item's normalised partial, then the last
+    // item of the request to arrive merges all of them.  Partials are written
+    // and read with agent-coherent (sc1) accesses, so items on different XCDs
+    // exchange them without writing back or invalidating whole L2 caches.
+    const uint32_t part_bytes = uint32_t(a.H) * kDV * 4;
+    if (head_ok) {
+      const float inv = 1.0f / l_tot;
+      const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.part_o + size_t(it) * a.H * kDV), (short)0, (int)part_bytes, 0x00020000);
+      const uint32_t rowoff = (uint32_t(head) * kDV + 4 * hi) * 4;
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v4;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * inv;
-            *reinterpret_cast<f32x4*>(op + 32 * cb + 8 * g) = v4;
+          for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * inv;
+          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, rowoff + (32 * cb + 8 * g) * 4, 0, kSc1);
+        }
+      if (hi == 0)
+        __hip_atomic_store(&a.part_lse[size_t(it) * a.H + head], lse2, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's partial is out
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_ticket = __hip_atomic_fetch_add(&a.ctr[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    if (ticket != cnt - 1) continue;
+    // every item of b has arrived: leave the counter ready for the next call
+    if (threadIdx.x == 0) __hip_atomic_store(&a.ctr[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!head_ok) continue;
+    // log-sum-exp merge (log2 domain): lse = log2 sum_s 2^lse_s,
+    // out = sum_s 2^(lse_s - lse) o_s, with o_s the normalised partials.
+    // The terms are summed in item order, and this item's own term is the
+    // very value it published, so the result does not depend on which item
+    // finished last.  One 32-column block of O at a time stays in VGPRs.
+    const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
+    auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
+    auto lse_of = [&](int slot) {
+      return slot == it ? lse2
+                        : __hip_atomic_load(&a.part_lse[size_t(slot) * a.H + head],
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float mlse = -INFINITY;
+    for (int s = 0; s < cnt; ++s) mlse = fmaxf(mlse, lse_of(slot_of(s)));
+    float lam = 0.0f;
+    for (int s = 0; s < cnt; ++s) lam += __builtin_amdgcn_exp2f(lse_of(slot_of(s)) - mlse);
+    const float inv = 1.0f / lam;
+    const float own_inv = 1.0f / l_tot;
+    __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) {
+      f32x16 acc = {};
+      for (int s = 0; s < cnt; ++s) {
+        const int slot = slot_of(s);
+        const float ws = __builtin_amdgcn_exp2f(lse_of(slot) - mlse) * inv;
+        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.part_o + size_t(slot) * a.H * kDV), (short)0, (int)part_bytes, 0x00020000);
+        const uint32_t rowoff = (uint32_t(head) * kDV + 4 * hi + 32 * cb) * 4;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4;
+          if (slot == it) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
+          } else {
+            v4 = __builtin_amdgcn_raw_buffer_load_b128(pr, rowoff + 8 * g * 4, 0, kSc1);
           }
-        if (hi == 0) a.part_lse[size_t(slot) * a.H + head] = lse_nat;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[4 * g + r] += ws * v4[r];
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = (__bf16)acc[4 * g + r];
+        *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = v4;
       }
     }
-    if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
+    if (hi == 0) a.lse[size_t(b) * a.H + head] = (mlse + log2f(lam)) * kLn2;
   }
 }
 
@@ -457,9 +615,12 @@ __device__ __forceinline__ int2 block_scan(int v, int* s_scan) {
   return r;
 }
 
+// Items are laid out full chunks first, then the last (shorter) chunk of each
+// request, then one item per empty request.
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
-    int ovh, int cap, int32_t* __restrict__ hdr, int4* __restrict__ req, int4* __restrict__ items) {
+    int ovh, int cap, int32_t* __restrict__ hdr, int4* __restrict__ req, int32_t* __restrict__ ctr,
+    int4* __restrict__ items) {
   __shared__ long long s_cost[kPlanThreads];
   __shared__ int s_chunk[kPlanThreads];
   __shared__ int s_scan[kPlanThreads];
@@ -477,7 +638,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
       const int nb = min(kPlanLens, B - b0);
       for (int i = tid; i < nb; i += kPlanThreads) s_len[i] = min(max(seq_lens[b0 + i], 0), Lmax);
       __syncthreads();
-      for (int i = 0; i < nb; ++i) n += (s_len[i] + T - 1) / T;
+      for (int i = 0; i < nb; ++i) n += max(1, (s_len[i] + T - 1) / T);
       __syncthreads();
     }
     s_cost[tid] = (n <= cap) ? ((n + n_slots - 1) / n_slots) * (long long)(T + ovh) : (1ll << 62);
@@ -500,111 +661,55 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     __syncthreads();
   }
 
-  // 2) totals: full chunks go first, remainders after them
-  int nf_loc = 0, nr_loc = 0, bad = 0;
+  // 2) totals: full chunks, remainders, empty requests
+  int nf_loc = 0, nr_loc = 0, ne_loc = 0, bad = 0;
   for (int b = tid; b < B; b += kPlanThreads) {
     const int L0 = seq_lens[b];
     if (L0 < 0 || L0 > Lmax) bad = 1;
     const int L = min(max(L0, 0), Lmax);
     nf_loc += L / chunk;
     nr_loc += (L % chunk) ? 1 : 0;
+    ne_loc += (L == 0) ? 1 : 0;
+    ctr[b] = 0;
   }
   const int NF = block_scan(nf_loc, s_scan).y;
   const int NR = block_scan(nr_loc, s_scan).y;
+  const int NE = block_scan(ne_loc, s_scan).y;
   const int any_bad = block_scan(bad, s_scan).y;
 
-  // 3) per-request placement from exclusive scans of (full count, remainder)
-  int carry_f = 0, carry_r = 0;
+  // 3) per-request placement from exclusive scans
+  int carry_f = 0, carry_r = 0, carry_e = 0;
   for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
     const int b = b0 + tid;
     const int L = (b < B) ? min(max(seq_lens[b], 0), Lmax) : 0;
     const int nf = L / chunk;
     const int nr = (L % chunk) ? 1 : 0;
+    const int ne = (b < B && L == 0) ? 1 : 0;
     const int2 fs = block_scan(nf, s_scan);
     const int2 rs = block_scan(nr, s_scan);
+    const int2 es = block_scan(ne, s_scan);
     if (b < B) {
       const int fbeg = carry_f + fs.x - nf;
       const int cnt = nf + nr;
       const int ritem = nr ? (NF + carry_r + rs.x - nr) : -1;
       req[b] = make_int4(fbeg, nf, ritem, cnt);
-      for (int s = 0; s < nf; ++s) {
-        const int idx = fbeg + s;
-        items[idx] = make_int4(b, s * chunk, (s + 1) * chunk, cnt > 1 ? idx : -1);
-      }
-      if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt > 1 ? ritem : -1);
+      for (int s = 0; s < nf; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
+      if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt);
+      if (ne) items[NF + NR + carry_e + es.x - 1] = make_int4(b, 0, 0, 0);
     }
     carry_f += fs.y;
     carry_r += rs.y;
+    carry_e += es.y;
   }
 
   // 4) header
   if (tid == 0) {
-    hdr[0] = NF + NR;
+    hdr[0] = NF + NR + NE;
     hdr[1] = chunk;
     hdr[2] = any_bad ? MLA_CHECK_SEQ_LEN_RANGE : 0;
     hdr[3] = 0;
     hdr[4] = NF;
   }
-}
-
-// ---------------------------------------------------------------------------
-// merge
-// ---------------------------------------------------------------------------
-constexpr int kMergeHeads = 8;  // heads per workgroup, 32 threads per head
-
-__global__ __launch_bounds__(256) void mla_merge_kernel(
-    __bf16* __restrict__ out, float* __restrict__ lse, int H,
-    const int4* __restrict__ req, const float* __restrict__ part_lse,
-    const float* __restrict__ part_o) {
-  const int b = blockIdx.x;
-  const int4 r = req[b];
-  const int cnt = r.w;
-  if (cnt == 1) return;
-  const int h = blockIdx.y * kMergeHeads + (threadIdx.x >> 5);
-  if (h >= H) return;
-  const int c0 = (threadIdx.x & 31) * 16;  // 16 columns per thread
-  __bf16* op = out + (size_t(b) * H + h) * kDV + c0;
-  if (cnt == 0) {
-    bf16x8 z = {};
-    *reinterpret_cast<bf16x8*>(op) = z;
-    *reinterpret_cast<bf16x8*>(op + 8) = z;
-    if ((threadIdx.x & 31) == 0) lse[size_t(b) * H + h] = -INFINITY;
-    return;
-  }
-  // items of this request: r.x .. r.x + r.y - 1, then r.z if >= 0
-  float m = -INFINITY;
-  for (int s = 0; s < cnt; ++s) {
-    const int slot = (s < r.y) ? r.x + s : r.z;
-    m = fmaxf(m, part_lse[size_t(slot) * H + h]);
-  }
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  float lam = 0.0f;
-  for (int s = 0; s < cnt; ++s) {
-    const int slot = (s < r.y) ? r.x + s : r.z;
-    const float wgt = expf(part_lse[size_t(slot) * H + h] - m);
-    lam += wgt;
-    const f32x4* src = reinterpret_cast<const f32x4*>(part_o + (size_t(slot) * H + h) * kDV + c0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 v = src[j];
-      acc[4 * j + 0] += wgt * v[0];
-      acc[4 * j + 1] += wgt * v[1];
-      acc[4 * j + 2] += wgt * v[2];
-      acc[4 * j + 3] += wgt * v[3];
-    }
-  }
-  const float inv = 1.0f / lam;
-  bf16x8 v0, v1;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    v0[j] = (__bf16)(acc[j] * inv);
-    v1[j] = (__bf16)(acc[8 + j] * inv);
-  }
-  *reinterpret_cast<bf16x8*>(op) = v0;
-  *reinterpret_cast<bf16x8*>(op + 8) = v1;
-  if ((threadIdx.x & 31) == 0) lse[size_t(b) * H + h] = m + logf(lam);
 }
 
 // ---------------------------------------------------------------------------
@@ -654,14 +759,14 @@ mla_status check_workspace(const void* ws, size_t ws_bytes, int B, int H) {
   return MLA_OK;
 }
 
-// Kernel variant for H heads: waves per workgroup and LDS stages.
+// Kernel variant for H heads: waves per workgroup, LDS stages, workgroups per CU.
 struct Variant {
   int nw, ns, wgs_per_cu;
 };
 Variant pick_variant(int H) {
   if (H > 64) return {4, 4, 1};
-  if (H > 32) return {2, 2, 2};
-  return {1, 2, 2};
+  if (H > 32) return {2, 4, 1};
+  return {1, 3, 1};
 }
 
 int item_overhead_tokens(int H) { return 32 + 2 * H; }
@@ -670,6 +775,39 @@ template <int NW, int NS>
 hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t st) {
   hipLaunchKernelGGL((mla_attend_kernel<NW, NS>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
+}
+
+mla_status validate_attend(const void* q, const void* latent_cache, const int32_t* block_table,
+                           float scale, const void* out, const float* lse, int32_t B, int32_t H,
+                           int32_t NB, int32_t BS, int32_t M, const void* workspace,
+                           size_t workspace_bytes) {
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (NB < 1) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !latent_cache || !block_table || !out || !lse) return MLA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4))
+    return MLA_ERR_ALIGNMENT;
+  if (!isfinite(scale)) return MLA_ERR_BAD_SCALE;
+  return check_workspace(workspace, workspace_bytes, B, H);
+}
+
+mla_status validate_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t M, int32_t BS,
+                         int32_t chunk_tokens, const void* workspace, size_t workspace_bytes) {
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (B == 0) return MLA_OK;
+  if (!seq_lens) return MLA_ERR_NULL_POINTER;
+  if (!aligned(seq_lens, 4)) return MLA_ERR_ALIGNMENT;
+  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  if (chunk_tokens < 0) return MLA_ERR_UNSUPPORTED;
+  if (chunk_tokens > 0) {
+    if (chunk_tokens % kSub) return MLA_ERR_UNSUPPORTED;
+    const long long per = ((long long)M * BS + chunk_tokens - 1) / chunk_tokens;
+    if ((long long)B * per > ws_layout(B, H).cap) return MLA_ERR_UNSUPPORTED;
+  }
+  return MLA_OK;
 }
 
 }  // namespace
@@ -684,27 +822,18 @@ size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS) {
 mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t M,
                            int32_t BS, int32_t chunk_tokens, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  mla_status s = check_sizes(B, H, M, BS);
-  if (s != MLA_OK) return s;
-  if (B == 0) return MLA_OK;
-  if (!seq_lens) return MLA_ERR_NULL_POINTER;
-  if (!aligned(seq_lens, 4)) return MLA_ERR_ALIGNMENT;
-  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
-  const WsLayout L = ws_layout(B, H);
-  if (chunk_tokens < 0) return MLA_ERR_UNSUPPORTED;
-  if (chunk_tokens > 0) {
-    if (chunk_tokens % kSub) return MLA_ERR_UNSUPPORTED;
-    const long long per = ((long long)M * BS + chunk_tokens - 1) / chunk_tokens;
-    if ((long long)B * per > L.cap) return MLA_ERR_UNSUPPORTED;
-  }
+  mla_status s = validate_plan(seq_lens, B, H, M, BS, chunk_tokens, workspace, workspace_bytes);
+  if (s != MLA_OK || B == 0) return s;
   int ncu = 0;
   if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  const WsLayout L = ws_layout(B, H);
   const Variant v = pick_variant(H);
   char* ws = static_cast<char*>(workspace);
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
                      seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.wgs_per_cu,
                      (int)chunk_tokens, item_overhead_tokens(H), L.cap,
                      reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
+                     reinterpret_cast<int32_t*>(ws + L.ctr_off),
                      reinterpret_cast<int4*>(ws + L.item_off));
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -713,16 +842,9 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              const int32_t* block_table, float scale, void* out, float* lse,
                              int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  mla_status s = check_sizes(B, H, M, BS);
-  if (s != MLA_OK) return s;
-  if (NB < 1) return MLA_ERR_BAD_SHAPE;
-  if (B == 0) return MLA_OK;
-  if (!q || !latent_cache || !block_table || !out || !lse) return MLA_ERR_NULL_POINTER;
-  if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-      !aligned(block_table, 4))
-    return MLA_ERR_ALIGNMENT;
-  if (!isfinite(scale)) return MLA_ERR_BAD_SCALE;
-  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
+                                 workspace, workspace_bytes);
+  if (s != MLA_OK || B == 0) return s;
   int ncu = 0;
   if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
   const WsLayout L = ws_layout(B, H);
@@ -734,6 +856,8 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
   a.out = static_cast<__bf16*>(out);
   a.lse = lse;
   a.hdr = reinterpret_cast<int32_t*>(ws);
+  a.req = reinterpret_cast<const int4*>(ws + L.req_off);
+  a.ctr = reinterpret_cast<int32_t*>(ws + L.ctr_off);
   a.items = reinterpret_cast<const int4*>(ws + L.item_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
   a.part_o = reinterpret_cast<float*>(ws + L.po_off);
@@ -749,29 +873,10 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
   hipError_t e;
   switch (v.nw) {
     case 4: e = launch_attend<4, 4>(a, grid, st); break;
-    case 2: e = launch_attend<2, 2>(a, grid, st); break;
-    default: e = launch_attend<1, 2>(a, grid, st); break;
+    case 2: e = launch_attend<2, 4>(a, grid, st); break;
+    default: e = launch_attend<1, 3>(a, grid, st); break;
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
-}
-
-mla_status mla_decode_merge(void* out, float* lse, int32_t B, int32_t H, int32_t M, int32_t BS,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  mla_status s = check_sizes(B, H, M, BS);
-  if (s != MLA_OK) return s;
-  if (B == 0) return MLA_OK;
-  if (!out || !lse) return MLA_ERR_NULL_POINTER;
-  if (!aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_ALIGNMENT;
-  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
-  const WsLayout L = ws_layout(B, H);
-  char* ws = static_cast<char*>(workspace);
-  dim3 grid(B, (H + kMergeHeads - 1) / kMergeHeads);
-  hipLaunchKernelGGL(mla_merge_kernel, grid, dim3(256), 0, (hipStream_t)stream,
-                     static_cast<__bf16*>(out), lse, (int)H,
-                     reinterpret_cast<const int4*>(ws + L.req_off),
-                     reinterpret_cast<const float*>(ws + L.plse_off),
-                     reinterpret_cast<const float*>(ws + L.po_off));
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status mla_decode(const void* q, const void* latent_cache, const int32_t* block_table,
@@ -779,23 +884,14 @@ mla_status mla_decode(const void* q, const void* latent_cache, const int32_t* bl
                       int32_t H, int32_t NB, int32_t BS, int32_t M, void* workspace,
                       size_t workspace_bytes, void* stream) {
   // Validate everything up front so that nothing is enqueued on failure.
-  mla_status s = check_sizes(B, H, M, BS);
-  if (s != MLA_OK) return s;
-  if (NB < 1) return MLA_ERR_BAD_SHAPE;
-  if (B == 0) return MLA_OK;
-  if (!q || !latent_cache || !block_table || !seq_lens || !out || !lse)
-    return MLA_ERR_NULL_POINTER;
-  if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4))
-    return MLA_ERR_ALIGNMENT;
-  if (!isfinite(scale)) return MLA_ERR_BAD_SCALE;
-  if ((s = check_workspace(workspace, workspace_bytes, B, H)) != MLA_OK) return s;
+  mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
+                                 workspace, workspace_bytes);
+  if (s != MLA_OK || B == 0) return s;
+  if ((s = validate_plan(seq_lens, B, H, M, BS, 0, workspace, workspace_bytes)) != MLA_OK) return s;
   if ((s = mla_decode_plan(seq_lens, B, H, M, BS, 0, workspace, workspace_bytes, stream)) != MLA_OK)
     return s;
-  if ((s = mla_decode_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
-                             workspace, workspace_bytes, stream)) != MLA_OK)
-    return s;
-  return mla_decode_merge(out, lse, B, H, M, BS, workspace, workspace_bytes, stream);
+  return mla_decode_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
+                           workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode_read_error(const void* workspace, int32_t* flags, void* stream) {

@@ -48,7 +48,7 @@ def test_abi_version_and_status_strings(L):
 def test_workspace_bytes(L):
     n = _lib.mla_decode_workspace_bytes(124, 128, 64, 64)
     cap = 124 + 1024
-    assert n >= cap * 128 * 512 * 4 + cap * 128 * 4 + cap * 16 + 124 * 16
+    assert n >= cap * 128 * 512 * 4 + cap * 128 * 4 + cap * 16 + 124 * 16 + 124 * 4
     assert n % 256 == 0
     assert _lib.mla_decode_workspace_bytes(2, 16, 7, 16) > 0
     # unsupported sizes give 0
@@ -99,7 +99,7 @@ def test_decode_rejects_bad_arguments_on_host(L):
     assert _decode(ws=FAKE + 128) == _lib.MLA_ERR_ALIGNMENT
 
 
-def test_plan_attend_merge_reject_bad_arguments_on_host(L):
+def test_plan_attend_reject_bad_arguments_on_host(L):
     P = _lib.mla_decode_plan
     assert P(FAKE, 0, 128, 7, 16, 0, FAKE, 1 << 40, None) == _lib.MLA_OK
     assert P(None, 2, 128, 7, 16, 0, FAKE, 1 << 40, None) == _lib.MLA_ERR_NULL_POINTER
@@ -116,9 +116,8 @@ def test_plan_attend_merge_reject_bad_arguments_on_host(L):
              None) == _lib.MLA_ERR_BAD_SCALE
     assert A(FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 2, 128, 0, 16, 7, FAKE, 1 << 40, None) \
         == _lib.MLA_ERR_BAD_SHAPE
-    Mg = _lib.mla_decode_merge
-    assert Mg(None, FAKE, 2, 128, 7, 16, FAKE, 1 << 40, None) == _lib.MLA_ERR_NULL_POINTER
-    assert Mg(FAKE, FAKE, 2, 128, 7, 16, FAKE, 4, None) == _lib.MLA_ERR_WORKSPACE
+    assert A(FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 2, 128, 14, 16, 7, FAKE, 4, None) \
+        == _lib.MLA_ERR_WORKSPACE
     assert _lib.lib().mla_decode_read_error(None, ctypes.byref(ctypes.c_int32()), None) \
         == _lib.MLA_ERR_NULL_POINTER
 

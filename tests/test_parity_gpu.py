@@ -39,7 +39,6 @@ def _run(w, chunk_tokens=None, ws=None):
         ws = ws or mla.Workspace(w.B, w.H, w.M, w.BS, dev)
         mla.plan(w.seq_lens, w.H, w.M, w.BS, ws, chunk_tokens=chunk_tokens)
         mla.attend(w.q, w.cache, w.block_table, w.scale, out, lse, ws)
-        mla.merge(out, lse, w.M, w.BS, ws)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -163,14 +162,13 @@ def test_run_to_run_determinism_and_plan_reuse():
     o1, l1 = _run(w, ws=ws)
     o2, l2 = _run(w, ws=ws)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
-    # one plan, two attend+merge calls (the queue counter must be back at 0)
+    # one plan, two attend calls (queue and arrival counters must be back at 0)
     out = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
     mla.plan(w.seq_lens, w.H, w.M, w.BS, ws)
     for _ in range(2):
         out.zero_()
         mla.attend(w.q, w.cache, w.block_table, w.scale, out, lse, ws)
-        mla.merge(out, lse, w.M, w.BS, ws)
         torch.cuda.synchronize()
         assert np.array_equal(out.float().cpu().numpy(), o1)
     assert ws.header()[3] == 0
