@@ -88,26 +88,27 @@ def cpu_baseline(w, budget_s: float):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     lens = w.seq_lens_list()
+    # host copies of each request's pages, fetched once outside the timed calls
+    host = []
+    for b in range(w.B):
+        nblk = -(-lens[b] // w.BS)
+        host.append((wl.bf16_bits(w.q[b:b + 1]), wl.bf16_bits(w.cache[w.block_table[b, :nblk].long()]),
+                     np.arange(nblk, dtype=np.int32)[None], np.array([lens[b]], dtype=np.int32)))
     done_tokens = 0
     done_req = 0
     elapsed = 0.0
-    for b in range(w.B):
-        L = lens[b]
-        nblk = -(-L // w.BS)
-        sub = wl.bf16_bits(w.cache[w.block_table[b, :nblk].long()])
-        qb = wl.bf16_bits(w.q[b:b + 1])
+    while elapsed < budget_s:
+        qb, sub, tab, ln = host[done_req % w.B]
         t0 = time.perf_counter()
-        orc.oracle_decode(qb, sub, np.arange(nblk, dtype=np.int32)[None],
-                          np.array([L], dtype=np.int32), w.scale)
+        orc.oracle_decode(qb, sub, tab, ln, w.scale)
         elapsed += time.perf_counter() - t0
-        done_tokens += L
+        done_tokens += int(ln[0])
         done_req += 1
-        if elapsed >= budget_s:
-            break
+    passes = done_req / w.B
     return {"value": done_tokens / elapsed, "unit": "cached-token reads/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done_req} of {w.B} requests ({done_tokens} tokens x {w.H} heads), "
-                      f"float64 NumPy, {elapsed:.1f} s"}
+            "sample": f"{done_req} request decodes ({passes:.1f} passes over the {w.B} requests, "
+                      f"{done_tokens} tokens x {w.H} heads), float64 NumPy, {elapsed:.1f} s"}
 
 
 def main():
