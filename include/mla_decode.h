@@ -73,12 +73,15 @@ typedef enum {
 /* Bits of the data-check word raised in the workspace (see mla_decode_read_error). */
 #define MLA_CHECK_SEQ_LEN_RANGE 1  /* some seq_lens[b] < 0 or > M*BS (clamped)       */
 #define MLA_CHECK_BLOCK_ID_RANGE 2 /* some used block id outside [0, NB) (set to 0)  */
+#define MLA_CHECK_MERGE_WAIT 4     /* a split merge stopped waiting for its partners
+                                      (never expected; outputs of that request are
+                                      unspecified)                                    */
 
 /* Bytes of workspace needed for a batch of B requests with H heads, a block
  * table of M entries per request and block size BS.  Returns 0 when the sizes
- * are outside the supported set.  The figure covers the work plan, one
- * arrival counter per request and fp32 split-KV partials for at most
- * B + 1024 work items. */
+ * are outside the supported set.  The figure covers the work plan, two
+ * counters per request and fp32 split-KV partials for at most B + 1024 work
+ * items. */
 size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS);
 
 /* Whole decode: the plan call followed by the attend call below.  The chunk
@@ -104,9 +107,10 @@ mla_status mla_decode(const void* q, const void* latent_cache,
  *   [3] work-queue counter (0 after the plan and after every attend call)
  *   [4] number of full items
  *   at byte 256: per request 4 words (first full item, full-item count,
- *   remainder item or -1, total item count); then, 256-byte aligned, one
- *   arrival counter per request (0 between calls); then per item 4 words
- *   (request, first token, end token, the request's item count). */
+ *   remainder item or -1, total item count); then, 256-byte aligned, two
+ *   counters per request (tickets taken, partials published; 0 between
+ *   calls); then per item 4 words (request, first token, end token, the
+ *   request's item count). */
 mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
                            int32_t M, int32_t BS, int32_t chunk_tokens,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -114,9 +118,11 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
 /* Step 2 — attention over every work item of the plan (the hot kernel), and
  * the split-KV merge.  An item that covers a whole request writes out/lse
  * directly; an empty request gets out = 0, lse = -inf.  When a request is
- * split, each of its items writes its normalised fp32 output and log-sum-exp
- * into the workspace, and the last of them to finish merges all of them:
+ * split, its items take tickets as they finish: every item but the last
+ * writes its normalised fp32 output and log-sum-exp into the workspace, and
+ * the last merges them with its own, summing in item order:
  * lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s (bf16, RNE).
+ * The result does not depend on which item finishes last.
  * Needs a plan made with the same B, H, M, BS. */
 mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              const int32_t* block_table, float scale,

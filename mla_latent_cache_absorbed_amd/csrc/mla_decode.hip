@@ -55,8 +55,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
+
+// Heads covered by one workgroup: 32 per wave, waves chosen from H.
+__host__ __device__ inline int heads_padded(int H) { return H > 64 ? 128 : H > 32 ? 64 : 32; }
 
 // Workspace sections (byte offsets).
 struct WsLayout {
@@ -68,13 +72,14 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_
 
 __host__ __device__ inline WsLayout ws_layout(int B, int H) {
   WsLayout w;
+  const int hp = heads_padded(H);
   w.cap = B + kMaxExtraItems;
   w.req_off = kHdrBytes;
   w.ctr_off = align256(w.req_off + size_t(B) * 16);
-  w.item_off = align256(w.ctr_off + size_t(B) * 4);
+  w.item_off = align256(w.ctr_off + size_t(B) * 8);
   w.plse_off = align256(w.item_off + size_t(w.cap) * 16);
-  w.po_off = align256(w.plse_off + size_t(w.cap) * H * 4);
-  w.total = align256(w.po_off + size_t(w.cap) * H * kDV * 4);
+  w.po_off = align256(w.plse_off + size_t(w.cap) * hp * 4);
+  w.total = align256(w.po_off + size_t(w.cap) * hp * kDV * 4);
   return w;
 }
 
@@ -149,10 +154,11 @@ struct AttendArgs {
   float* lse;
   int32_t* hdr;          // workspace header (n_items, chunk, check bits, queue)
   const int4* req;       // per request: first full item, full count, remainder item, count
-  int32_t* ctr;          // per request: arrivals of split items (0 between calls)
+  int32_t* ctr;          // per request: [tickets taken, partials published] (0 between calls)
   const int4* items;     // per item: request, first token, end token, request's item count
-  float* part_lse;       // [cap, H]  log2-domain log-sum-exp of each split item
-  float* part_o;         // [cap, H, 512] normalised output of each split item
+  float* part_lse;       // [cap, Hp]  log2-domain log-sum-exp of each split item
+  float* part_o;         // [cap, Hp * 512] normalised output of each split item, in the
+                         // accumulator layout of the waves (see the epilogue)
   float scale_log2;      // scale * log2(e)
   int32_t B, H, NB, M, lgBS;
 };
@@ -227,6 +233,13 @@ __device__ __forceinline__ void issue_stage(const AttendArgs& a, char LDS_AS* sb
   }
 }
 
+template <bool V>
+struct BoolC {
+  static constexpr bool value = V;
+};
+
+constexpr int kMergeSpinLimit = 1 << 22;  // polls for the partners of a split merge
+
 template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
@@ -238,12 +251,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 
   constexpr int LPW = kLoadsPerStage / NW;  // loads per wave per stage
   constexpr int PF = 3;                     // operand reads in flight per MFMA stream
+  constexpr int HP = NW * 32;               // heads covered by the workgroup
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int hl = lane & 31;
   const int hi = lane >> 5;
   const int head = w * 32 + hl;
   const bool head_ok = head < a.H;
+  const float c2 = a.scale_log2;
   const int n_items = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[0]);
   // lanes l and l^32 hold the same head: exchange through ds_bpermute
   const int xlane = (lane ^ 32) << 2;
@@ -301,14 +316,20 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 
     if (t1 <= t0) {
       // a request with no cached tokens: out = 0, lse = -inf
-      if (head_ok) {
-        __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
-        const bf16x4 z = {};
+      int lane_z = lane;
+      asm volatile("" : "+v"(lane_z));
+      const int head_z = w * 32 + (lane_z & 31);
+      if (head_z < a.H) {
+        const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.out + (size_t(b) * a.H + w * 32) * kDV), (short)0,
+            (a.H - w * 32) * kDV * 2, 0x00020000);
+        const uint32_t zoff = uint32_t((lane_z & 31) * kDV + 4 * (lane_z >> 5)) * 2;
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = z;
-        if (hi == 0) a.lse[size_t(b) * a.H + head] = -INFINITY;
+          for (int g = 0; g < 4; ++g)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, zr, zoff + (32 * cb + 8 * g) * 2, 0, 0);
+        if ((lane_z >> 5) == 0) a.lse[size_t(b) * a.H + head_z] = -INFINITY;
       }
       continue;
     }
@@ -318,9 +339,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     f32x16 o[16];
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
-    float m_run = -INFINITY;   // exponent reference of this head (log2 units)
-    float m_seen = -INFINITY;  // largest scaled score seen
-    float l_run = 0.0f;        // this lane's share of the row sum
+    float m_run = -INFINITY;  // exponent reference of this head (log2 units)
+    float amax = -INFINITY;   // largest exponent argument (score * c2 - m_run) of this lane
+    float la = 0.0f, lb = 0.0f;  // this lane's share of the row sum, in two chains
 
 #define MLA_KREAD(sb, s)                                                               \
   ((s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))      \
@@ -336,45 +357,22 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
   } while (0)
 
-    // Scale scores to the exp2 domain, mask tokens >= t1; return the per-head
-    // max (lanes l and l^32 hold the same head and combine their halves).
-    auto stage_max = [&](f32x16& sacc, int base) -> float {
-      // register v holds token base + 4hi + 8(v/4) + (v%4): valid while
-      // 8(v/4) + (v%4) < t1 - base - 4hi
-      const int lim = t1 - base - 4 * hi;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = (8 * (v >> 2) + (v & 3) < lim) ? sacc[v] * a.scale_log2 : -INFINITY;
-        sacc[v] = x;
-        mx = fmaxf(mx, x);
-      }
-      return pair_max(mx);
-    };
-    // P = 2^(S - m_run) as bf16 MFMA operands (tokens 0-15 in p0, 16-31 in p1).
-    auto stage_p = [&](const f32x16& sacc, bf16x8& p0, bf16x8& p1) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = __builtin_amdgcn_exp2f(sacc[v] - m_run);
-        l_run += pv;
-        if (v < 8) p0[v] = (__bf16)pv;
-        else p1[v - 8] = (__bf16)pv;
-      }
-    };
-
     // ---- stage pipeline ----
     // Each head's exponent reference m_run is fixed from the item's first
     // stage (where O is still zero), so O is never rescaled: P = 2^(s - m_run)
     // may grow up to 2^kRefHeadroom on later stages, which fp32 sums and bf16
-    // weights carry exactly in relative terms.  If a later score exceeds the
-    // reference by more than that (not seen with attention-like data), the
-    // whole item is redone with the larger reference.
+    // weights carry exactly in relative terms.  Each lane tracks the largest
+    // exponent argument it produced; if one exceeds the headroom (not seen
+    // with attention-like data), the whole item is redone with the larger
+    // reference.  With the reference fixed, a stage's weights need no
+    // cross-lane step, so its softmax runs in the shadow of MFMAs.
     //
-    // Iteration k holds P(k) and runs the score MFMAs of stage k+1
-    // interleaved with the weighted-sum MFMAs of stage k; stages k+2 ..
-    // k+NS-2 stay in flight.
+    // Iteration k holds P(k).  Phase 1 runs the 36 score MFMAs of stage k+1
+    // interleaved with the first 16 weighted-sum MFMAs of stage k; phase 2
+    // runs the other 16 with the softmax of stage k+1 between them.  Stages
+    // k+2 .. k+NS-2 stay in flight.  Only a request's last stage can be
+    // partial, so only the last iteration applies the length mask.
     for (;;) {
-      bool over = false;
       // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
       // lane holds head hl, dims 16s + 8hi .. +7 (reloaded on a redo so that
       // they are not live past the last score MFMA of a pass).
@@ -411,15 +409,33 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         }
         qk_drain(sacc);
       }
+      // register v holds token 4hi + 8(v/4) + (v%4) of its stage: valid
+      // while 8(v/4) + (v%4) < (stage end) - 4hi
       bf16x8 p0, p1;
       {
-        const float mx = stage_max(sacc, t0);
-        m_seen = fmaxf(m_seen, mx);
-        if (m_run == -INFINITY) m_run = mx;
-        over |= mx > m_run + kRefHeadroom;
-        stage_p(sacc, p0, p1);
+        const int lim = t1 - t0 - 4 * hi;
+        if (m_run == -INFINITY) {
+          // first pass: the reference is the head's largest stage-0 score
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, sacc[v] * c2);
+          m_run = pair_max(mx);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float arg = (8 * (v >> 2) + (v & 3) < lim) ? fmaf(sacc[v], c2, -m_run) : -INFINITY;
+          amax = fmaxf(amax, arg);
+          const float pv = __builtin_amdgcn_exp2f(arg);
+          if (v & 1) lb += pv;
+          else la += pv;
+          if (v < 8) p0[v] = (__bf16)pv;
+          else p1[v - 8] = (__bf16)pv;
+        }
       }
-      for (int k = 0; k + 1 < nst; ++k) {
+
+      auto iteration = [&](int k, auto mask_tag) {
+        constexpr bool kMask = decltype(mask_tag)::value;
         const char LDS_AS* sbv = lds + (k % NS) * kStageBytes;
         // stage k+1 must be in LDS; stage k+2 may still be loading
         if (k + 2 < nst) wait_vmcnt_lgkm0<LPW * (NS - 3)>();
@@ -435,22 +451,42 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           kf[s] = MLA_KREAD(sbk, s);
           MLA_VREAD(sbv, s, vf[s]);
         }
+        // phase 1
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
           if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
           else qk_mfma(sacc, kf[s % PF], qreg[s]);
           if (s + PF < 36) kf[s % PF] = MLA_KREAD(sbk, s + PF);
-          if (s < 32) {
-            pv_mfma(o[s & 15], vf[s % PF], (s >> 4) ? p1 : p0);
-            if (s + PF < 32) MLA_VREAD(sbv, s + PF, vf[s % PF]);
+          if (s < 32 && (s & 1)) {
+            const int n = s >> 1;
+            pv_mfma(o[n], vf[n % PF], p0);
+            MLA_VREAD(sbv, n + PF, vf[n % PF]);
           }
         }
         qk_drain(sacc);
-        const float mx = stage_max(sacc, t0 + (k + 1) * kSub);
-        m_seen = fmaxf(m_seen, mx);
-        over |= mx > m_run + kRefHeadroom;
-        stage_p(sacc, p0, p1);
-      }
+        // phase 2
+        const int lim = t1 - (t0 + (k + 1) * kSub) - 4 * hi;
+        bf16x8 n0, n1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int n = 16 + v;
+          pv_mfma(o[v], vf[n % PF], p1);
+          if (n + PF < 32) MLA_VREAD(sbv, n + PF, vf[n % PF]);
+          float arg = fmaf(sacc[v], c2, -m_run);
+          if (kMask) arg = (8 * (v >> 2) + (v & 3) < lim) ? arg : -INFINITY;
+          amax = fmaxf(amax, arg);
+          const float pv = __builtin_amdgcn_exp2f(arg);
+          if (v & 1) lb += pv;
+          else la += pv;
+          if (v < 8) n0[v] = (__bf16)pv;
+          else n1[v - 8] = (__bf16)pv;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        p0 = n0;
+        p1 = n1;
+      };
+      for (int k = 0; k + 2 < nst; ++k) iteration(k, BoolC<false>{});
+      if (nst >= 2) iteration(nst - 2, BoolC<true>{});
       {
         // weighted sum of the last stage
         const char LDS_AS* sbv = lds + ((nst - 1) % NS) * kStageBytes;
@@ -465,10 +501,13 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       }
       // All waves are done reading the ring before it is refilled.
       block_barrier();
-      if (!__syncthreads_or(over)) break;
-      // Redo the item from its first stage with the larger reference.
-      m_run = m_seen;
-      l_run = 0.0f;
+      if (!__syncthreads_or(amax > kRefHeadroom)) break;
+      // Redo the item from its first stage with the head's largest score as
+      // the reference.
+      m_run += pair_max(amax);
+      amax = -INFINITY;
+      la = 0.0f;
+      lb = 0.0f;
       pv_drain(o);
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
@@ -479,87 +518,171 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
 
     // ---- finalize ----
-    const float l_tot = pair_sum(l_run);
+    // Per-lane offsets of the epilogue derive from an opaque copy of the
+    // lane index, so that none of them is hoisted out of the item loop and
+    // kept live (or spilled) across the stage pipeline.
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int hl_e = lane_e & 31;
+    const int hi_e = lane_e >> 5;
+    const int head_e = w * 32 + hl_e;
+    const float l_tot = pair_sum(la + lb);
     const float lse2 = m_run + log2f(l_tot);  // log2 of sum_t 2^(scaled score)
+    const float own_inv = 1.0f / l_tot;
+    // out and lse of request b through buffer resources (32-bit lane offsets)
+    const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
+    const uint32_t out_off = uint32_t(head_e * kDV + 4 * hi_e) * 2;
+    // bf16 of 4 consecutive columns 32cb + 8g + 4hi .. +3 of this lane's head
+    auto store_out4 = [&](int cb, int g, const float (&v)[4]) {
+      bf16x4 h4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h4[r] = (__bf16)v[r];
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
+                                            out_off + (32 * cb + 8 * g) * 2, 0, 0);
+    };
     if (cnt == 1) {
       if (head_ok) {
-        const float inv = 1.0f / l_tot;
-        __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            bf16x4 v4;
+            float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = (__bf16)(o[cb][4 * g + r] * inv);
-            *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = v4;
+            for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * g + r] * own_inv;
+            store_out4(cb, g, v);
           }
-        if (hi == 0) a.lse[size_t(b) * a.H + head] = lse2 * kLn2;
+        if (hi_e == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2), lse_r, head_e * 4, 0, 0);
       }
       continue;
     }
 
-    // Split request: publish this item's normalised partial, then the last
-    // item of the request to arrive merges all of them.  Partials are written
-    // and read with agent-coherent (sc1) accesses, so items on different XCDs
-    // exchange them without writing back or invalidating whole L2 caches.
-    const uint32_t part_bytes = uint32_t(a.H) * kDV * 4;
-    if (head_ok) {
-      const float inv = 1.0f / l_tot;
-      const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.part_o + size_t(it) * a.H * kDV), (short)0, (int)part_bytes, 0x00020000);
-      const uint32_t rowoff = (uint32_t(head) * kDV + 4 * hi) * 4;
+    // Split request.  The item takes its ticket first: all but the last item
+    // of the request publish their normalised partial and wait no further;
+    // the last waits until they have all published and merges.  Partials are
+    // stored in the waves' accumulator layout (each store instruction writes
+    // 1 KB contiguous; the merging wave reads back the same lanes' values),
+    // with agent-coherent (sc1) accesses, so items on different XCDs exchange
+    // them without writing back or invalidating whole L2 caches.
+    if (threadIdx.x == 0)
+      s_ticket = __hip_atomic_fetch_add(&a.ctr[2 * b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    constexpr int kWaveBytes = 32 * kDV * 4;  // one wave's share of a partial
+    auto part_rsrc = [&](int slot) {
+      return __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.part_o + (size_t(slot) * HP + w * 32) * kDV), (short)0, kWaveBytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
+    const uint32_t lane_off = uint32_t(lane_e) * 16;
+    if (ticket != cnt - 1) {
+      const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * inv;
-          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, rowoff + (32 * cb + 8 * g) * 4, 0, kSc1);
+          for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
+          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
         }
-      if (hi == 0)
-        __hip_atomic_store(&a.part_lse[size_t(it) * a.H + head], lse2, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      if (hi_e == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's partial is out
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&a.ctr[2 * b + 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
     }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's partial is out
+    // The last item: its partners all took their tickets earlier, so they
+    // are past their stage loops and only have stores left; the wait ends.
+    // It is bounded all the same, and a flag is raised if the bound is hit.
+    if (threadIdx.x == 0) {
+      for (int spin = 0;; ++spin) {
+        if (__hip_atomic_load(&a.ctr[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cnt - 1)
+          break;
+        if (spin >= kMergeSpinLimit) {
+          atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      // leave both counters ready for the next call
+      __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&a.ctr[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
-    if (ticket != cnt - 1) continue;
-    // every item of b has arrived: leave the counter ready for the next call
-    if (threadIdx.x == 0) __hip_atomic_store(&a.ctr[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!head_ok) continue;
     // log-sum-exp merge (log2 domain): lse = log2 sum_s 2^lse_s,
     // out = sum_s 2^(lse_s - lse) o_s, with o_s the normalised partials.
-    // The terms are summed in item order, and this item's own term is the
-    // very value it published, so the result does not depend on which item
-    // finished last.  One 32-column block of O at a time stays in VGPRs.
+    // Terms are summed in item order (out = fma(w_s, o_s, acc) from acc = 0),
+    // and this item's own term is the very value it would have published, so
+    // the result does not depend on which item finished last.
     const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
     auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
     auto lse_of = [&](int slot) {
       return slot == it ? lse2
-                        : __hip_atomic_load(&a.part_lse[size_t(slot) * a.H + head],
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                              plse_r, uint32_t(slot * HP + head_e) * 4, 0, kSc1));
     };
+    if (cnt == 2) {
+      // the common split: one partner, whose loads are all independent
+      const int s0 = slot_of(0), s1 = slot_of(1);
+      const float l0 = lse_of(s0), l1 = lse_of(s1);
+      const float mlse = fmaxf(l0, l1);
+      const float e0 = __builtin_amdgcn_exp2f(l0 - mlse), e1 = __builtin_amdgcn_exp2f(l1 - mlse);
+      const float lam = e0 + e1;
+      const float inv = 1.0f / lam;
+      const float w0 = e0 * inv, w1 = e1 * inv;
+      const bool own_first = s0 == it;
+      const __amdgpu_buffer_rsrc_t pr = part_rsrc(own_first ? s1 : s0);
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float own = o[cb][4 * g + r] * own_inv;
+            v[r] = own_first ? fmaf(w1, x[r], w0 * own) : fmaf(w1, own, w0 * x[r]);
+          }
+          if (head_ok) store_out4(cb, g, v);
+        }
+      if (head_ok && hi_e == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, head_e * 4, 0, 0);
+      continue;
+    }
+    // General split: per-item weights of this wave's heads go to the LDS
+    // ring (free now), 32 floats per item, for up to kSlotsLds items.
+    constexpr int kSlotsLds = NS * kStageBytes / (NW * 32 * 4);
+    float LDS_AS* wsl = (float LDS_AS*)(lds) + w * 32 * kSlotsLds + hl_e;
+    const bool in_lds = cnt <= kSlotsLds;
     float mlse = -INFINITY;
-    for (int s = 0; s < cnt; ++s) mlse = fmaxf(mlse, lse_of(slot_of(s)));
+    for (int s = 0; s < cnt; ++s) {
+      const float l = lse_of(slot_of(s));
+      mlse = fmaxf(mlse, l);
+      if (in_lds) wsl[32 * s] = l;
+    }
     float lam = 0.0f;
-    for (int s = 0; s < cnt; ++s) lam += __builtin_amdgcn_exp2f(lse_of(slot_of(s)) - mlse);
+    for (int s = 0; s < cnt; ++s) {
+      const float e = __builtin_amdgcn_exp2f((in_lds ? wsl[32 * s] : lse_of(slot_of(s))) - mlse);
+      lam += e;
+      if (in_lds) wsl[32 * s] = e;
+    }
     const float inv = 1.0f / lam;
-    const float own_inv = 1.0f / l_tot;
-    __bf16* op = a.out + (size_t(b) * a.H + head) * kDV + 4 * hi;
+    auto weight = [&](int s) {
+      return (in_lds ? wsl[32 * s] : __builtin_amdgcn_exp2f(lse_of(slot_of(s)) - mlse)) * inv;
+    };
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) {
       f32x16 acc = {};
       for (int s = 0; s < cnt; ++s) {
         const int slot = slot_of(s);
-        const float ws = __builtin_amdgcn_exp2f(lse_of(slot) - mlse) * inv;
-        const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.part_o + size_t(slot) * a.H * kDV), (short)0, (int)part_bytes, 0x00020000);
-        const uint32_t rowoff = (uint32_t(head) * kDV + 4 * hi + 32 * cb) * 4;
+        const float ws = weight(s);
+        const __amdgpu_buffer_rsrc_t pr = part_rsrc(slot);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v4;
@@ -567,21 +690,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
           } else {
-            v4 = __builtin_amdgcn_raw_buffer_load_b128(pr, rowoff + 8 * g * 4, 0, kSc1);
+            v4 = __builtin_amdgcn_raw_buffer_load_b128(pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[4 * g + r] += ws * v4[r];
+          for (int r = 0; r < 4; ++r) acc[4 * g + r] = fmaf(ws, v4[r], acc[4 * g + r]);
         }
       }
+      if (head_ok)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = (__bf16)acc[4 * g + r];
-        *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * g) = v4;
-      }
+        for (int g = 0; g < 4; ++g) {
+          const float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+          store_out4(cb, g, v);
+        }
     }
-    if (hi == 0) a.lse[size_t(b) * a.H + head] = (mlse + log2f(lam)) * kLn2;
+    if (head_ok && hi_e == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, head_e * 4, 0, 0);
   }
 }
 
@@ -670,7 +793,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     nf_loc += L / chunk;
     nr_loc += (L % chunk) ? 1 : 0;
     ne_loc += (L == 0) ? 1 : 0;
-    ctr[b] = 0;
+    ctr[2 * b] = 0;
+    ctr[2 * b + 1] = 0;
   }
   const int NF = block_scan(nf_loc, s_scan).y;
   const int NR = block_scan(nr_loc, s_scan).y;
