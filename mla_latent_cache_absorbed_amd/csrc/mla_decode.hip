@@ -179,57 +179,67 @@ __device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t 
                                              const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(r), "{m0}"(m0) : "memory");
+               :: "v"(voff), "s"(r), "{m0}"(m0));
 }
 __device__ __forceinline__ void dma16_global(const char* src, const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "{m0}"(m0) : "memory");
+               :: "v"(src), "{m0}"(m0));
 }
 
-// Issue this wave's share of the direct-to-LDS loads of one stage (32/NW
-// region-A rows and 4/NW region-B loads).  Tokens past `t1` are clamped to
-// t1-1, a row of the request that is always valid; the softmax masks them.
+// Physical blocks of one 32-token stage (wave-uniform).  base is a multiple
+// of 32 and BS >= 16, so a stage spans at most two blocks.
+struct StageIds {
+  int base;        // first token of the stage
+  int lb0;         // logical block of the first token
+  int blk0, blk1;  // physical blocks of the first and the last token
+};
+
+// Reads the block ids of the stage starting at `base` (scalar loads of a
+// table that is constant during the kernel).  Ids outside [0, NB) are
+// replaced by 0 and flagged.
+__device__ __forceinline__ StageIds stage_ids(const AttendArgs& a, int b, int base, int t1,
+                                              int& bad) {
+  const CONST_AS int32_t* trow = (const CONST_AS int32_t*)(a.table) + size_t(b) * a.M;
+  StageIds s;
+  s.base = base;
+  s.lb0 = base >> a.lgBS;
+  const int lb1 = min(base + kSub - 1, t1 - 1) >> a.lgBS;
+  s.blk0 = trow[s.lb0];
+  s.blk1 = trow[lb1];
+  if ((unsigned)s.blk0 >= (unsigned)a.NB) { s.blk0 = 0; bad = 1; }
+  if ((unsigned)s.blk1 >= (unsigned)a.NB) { s.blk1 = 0; bad = 1; }
+  return s;
+}
+
+// Issues load j (of 36/NW) of this wave's share of a stage: rows w, w+NW, ...
+// of region A (one 1 KB kv_c row each), then region-B loads (k_rope chunks
+// 2jb, 2jb+1 of all 32 tokens).  Tokens past t1 are clamped to t1-1, a row
+// of the request that is always valid; the softmax masks them.
 template <int NW>
-__device__ __forceinline__ void issue_stage(const AttendArgs& a, char LDS_AS* sbuf, int b,
-                                            int base, int t1, int w, int lane, int& bad) {
+__device__ __forceinline__ void issue_load(const AttendArgs& a, const StageIds& id,
+                                           char LDS_AS* sbuf, int t1, int w, uint32_t lane16,
+                                           int j) {
   const int lg = a.lgBS;
   const int bs_mask = (1 << lg) - 1;
-  const uint32_t blk_bytes = uint32_t(kD * 2) << lg;
-  // uniform reads of a table that is constant during the kernel: scalar loads
-  const CONST_AS int32_t* trow = (const CONST_AS int32_t*)(a.table) + size_t(b) * a.M;
   const int last = t1 - 1;
-  // base is a multiple of 32 and BS >= 16: at most two blocks per stage
-  const int lb0 = base >> lg;
-  const int lb1 = min(base + kSub - 1, last) >> lg;
-  int blk0 = trow[lb0];
-  int blk1 = trow[lb1];
-  if ((unsigned)blk0 >= (unsigned)a.NB) { blk0 = 0; bad = 1; }
-  if ((unsigned)blk1 >= (unsigned)a.NB) { blk1 = 0; bad = 1; }
   const char* cbase = reinterpret_cast<const char*>(a.cache);
-  const __amdgpu_buffer_rsrc_t r0 = block_rsrc(cbase, blk0, blk_bytes);
-  const __amdgpu_buffer_rsrc_t r1 = block_rsrc(cbase, blk1, blk_bytes);
-  uint32_t lane16 = uint32_t(lane) * 16;
-  // Keep the per-lane load offsets from being hoisted out of the item loop
-  // (they would be spilled and reloaded with a full vmcnt wait).
-  asm volatile("" : "+v"(lane16));
-#pragma unroll
-  for (int k = 0; k < kSub / NW; ++k) {
-    const int i = w + NW * k;                 // region-A row, wave-uniform
-    const int tok = min(base + i, last);
+  if (j < kSub / NW) {
+    const int i = w + NW * j;  // region-A row, wave-uniform
+    const int tok = min(id.base + i, last);
+    const uint32_t blk_bytes = uint32_t(kD * 2) << lg;
+    const __amdgpu_buffer_rsrc_t r =
+        block_rsrc(cbase, ((tok >> lg) == id.lb0) ? id.blk0 : id.blk1, blk_bytes);
     const uint32_t voff = uint32_t(tok & bs_mask) * (kD * 2) + (lane16 ^ uint32_t(swzA(i) * 16));
-    dma16_buffer(((tok >> lg) == lb0) ? r0 : r1, voff, sbuf + i * 1024);
-  }
-#pragma unroll
-  for (int k = 0; k < 4 / NW; ++k) {
-    const int j = w + NW * k;                 // region-B load: chunks 2j, 2j+1
+    dma16_buffer(r, voff, sbuf + i * 1024);
+  } else {
+    const int jb = w + NW * (j - kSub / NW);  // region-B load: chunks 2jb, 2jb+1
     const int t = (lane16 >> 4) & 31;
-    const int cp = 2 * j + (lane16 >> 9);
-    const int tok = min(base + t, last);
-    const int blk = ((tok >> lg) == lb0) ? blk0 : blk1;
+    const int cp = 2 * jb + (lane16 >> 9);
+    const int tok = min(id.base + t, last);
+    const int blk = ((tok >> lg) == id.lb0) ? id.blk0 : id.blk1;
     const size_t row = (size_t(blk) << lg) | size_t(tok & bs_mask);
-    const char* src = cbase + row * (kD * 2) + 1024 + cp * 16;
-    dma16_global(src, sbuf + kRegionB + j * 1024);
+    dma16_global(cbase + row * (kD * 2) + 1024 + cp * 16, sbuf + kRegionB + jb * 1024);
   }
 }
 
@@ -250,7 +260,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   char LDS_AS* lds = (char LDS_AS*)(lds_raw);
 
   constexpr int LPW = kLoadsPerStage / NW;  // loads per wave per stage
-  constexpr int PF = 3;                     // operand reads in flight per MFMA stream
+  constexpr int PFK = 4;                    // score operand reads in flight
+  constexpr int PFV = 2;                    // weighted-sum operand reads in flight
   constexpr int HP = NW * 32;               // heads covered by the workgroup
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -368,10 +379,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // cross-lane step, so its softmax runs in the shadow of MFMAs.
     //
     // Iteration k holds P(k).  Phase 1 runs the 36 score MFMAs of stage k+1
-    // interleaved with the first 16 weighted-sum MFMAs of stage k; phase 2
-    // runs the other 16 with the softmax of stage k+1 between them.  Stages
-    // k+2 .. k+NS-2 stay in flight.  Only a request's last stage can be
-    // partial, so only the last iteration applies the length mask.
+    // interleaved with the first 16 weighted-sum MFMAs of stage k, and issues
+    // this wave's loads of stage k+NS-1 spread between them; phase 2 runs the
+    // other 16 weighted-sum MFMAs with the softmax of stage k+1 between them.
+    // Stages k+2 .. k+NS-2 stay in flight.  Every iteration issues a full
+    // stage (past the item's end, a copy of its last stage into a free slot)
+    // so that one wait count serves all iterations.  Only a request's last
+    // stage can be partial, so only the last iteration applies the mask.
+    uint32_t lane16 = uint32_t(lane) * 16;
+    // keep the per-lane load offsets from being hoisted out of the item loop
+    asm volatile("" : "+v"(lane16));
+    auto stage_base = [&](int p) { return t0 + min(p, nst - 1) * kSub; };
     for (;;) {
       // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
       // lane holds head hl, dims 16s + 8hi .. +7 (reloaded on a redo so that
@@ -388,30 +406,34 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         }
       }
 #pragma unroll
-      for (int p = 0; p < NS - 1; ++p)
-        if (p < nst) issue_stage<NW>(a, lds + p * kStageBytes, b, t0 + p * kSub, t1, w, lane, bad);
+      for (int p = 0; p < NS - 1; ++p) {
+        const StageIds id = stage_ids(a, b, stage_base(p), t1, bad);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j)
+          issue_load<NW>(a, id, lds + p * kStageBytes, t1, w, lane16, j);
+      }
+      StageIds nxt = stage_ids(a, b, stage_base(NS - 1), t1, bad);
       // stage 0 scores (a lone chain, once per item)
-      if (nst >= NS - 1) wait_vmcnt_lgkm0<LPW * (NS - 2)>();
-      else if (nst == 2) wait_vmcnt_lgkm0<LPW>();
-      else wait_vmcnt_lgkm0<0>();
+      wait_vmcnt_lgkm0<LPW * (NS - 2)>();
       block_barrier();
       f32x16 sacc;
       {
         const char LDS_AS* sb = lds;
-        bf16x8 kf[PF];
+        bf16x8 kf[PFK];
 #pragma unroll
-        for (int s = 0; s < PF; ++s) kf[s] = MLA_KREAD(sb, s);
+        for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sb, s);
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
           if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
-          else qk_mfma(sacc, kf[s % PF], qreg[s]);
-          if (s + PF < 36) kf[s % PF] = MLA_KREAD(sb, s + PF);
+          else qk_mfma(sacc, kf[s % PFK], qreg[s]);
+          if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sb, s + PFK);
         }
         qk_drain(sacc);
       }
       // register v holds token 4hi + 8(v/4) + (v%4) of its stage: valid
       // while 8(v/4) + (v%4) < (stage end) - 4hi
       bf16x8 p0, p1;
+      bf16x8 vf[PFV];  // weighted-sum operands, read one phase ahead
       {
         const int lim = t1 - t0 - 4 * hi;
         if (m_run == -INFINITY) {
@@ -432,35 +454,41 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           if (v < 8) p0[v] = (__bf16)pv;
           else p1[v - 8] = (__bf16)pv;
         }
+#pragma unroll
+        for (int s = 0; s < PFV; ++s) MLA_VREAD(lds, s, vf[s]);
       }
 
       auto iteration = [&](int k, auto mask_tag) {
         constexpr bool kMask = decltype(mask_tag)::value;
+        constexpr int kDmaEvery = 36 / LPW;  // score MFMAs per load issued
         const char LDS_AS* sbv = lds + (k % NS) * kStageBytes;
         // stage k+1 must be in LDS; stage k+2 may still be loading
-        if (k + 2 < nst) wait_vmcnt_lgkm0<LPW * (NS - 3)>();
-        else wait_vmcnt_lgkm0<0>();
+        wait_vmcnt_lgkm0<LPW * (NS - 3)>();
         block_barrier();
-        if (k + NS - 1 < nst)
-          issue_stage<NW>(a, lds + ((k + NS - 1) % NS) * kStageBytes, b,
-                          t0 + (k + NS - 1) * kSub, t1, w, lane, bad);
+        const StageIds cur = nxt;
+        char LDS_AS* sdst = lds + ((k + NS - 1) % NS) * kStageBytes;
+        nxt = stage_ids(a, b, stage_base(k + NS), t1, bad);
         const char LDS_AS* sbk = lds + ((k + 1) % NS) * kStageBytes;
-        bf16x8 kf[PF], vf[PF];
+        bf16x8 kf[PFK];
 #pragma unroll
-        for (int s = 0; s < PF; ++s) {
-          kf[s] = MLA_KREAD(sbk, s);
-          MLA_VREAD(sbv, s, vf[s]);
+        for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sbk, s);
+        // phase 1: two weighted-sum MFMAs (operands already in registers)
+        // cover the first score reads; then score, score, weighted-sum ...
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          pv_mfma(o[n], vf[n % PFV], p0);
+          MLA_VREAD(sbv, n + PFV, vf[n % PFV]);
         }
-        // phase 1
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
           if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
-          else qk_mfma(sacc, kf[s % PF], qreg[s]);
-          if (s + PF < 36) kf[s % PF] = MLA_KREAD(sbk, s + PF);
-          if (s < 32 && (s & 1)) {
-            const int n = s >> 1;
-            pv_mfma(o[n], vf[n % PF], p0);
-            MLA_VREAD(sbv, n + PF, vf[n % PF]);
+          else qk_mfma(sacc, kf[s % PFK], qreg[s]);
+          if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sbk, s + PFK);
+          if (s % kDmaEvery == 0) issue_load<NW>(a, cur, sdst, t1, w, lane16, s / kDmaEvery);
+          if ((s & 1) && (s >> 1) + 2 < 16) {
+            const int n = (s >> 1) + 2;
+            pv_mfma(o[n], vf[n % PFV], p0);
+            MLA_VREAD(sbv, n + PFV, vf[n % PFV]);
           }
         }
         qk_drain(sacc);
@@ -470,8 +498,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int n = 16 + v;
-          pv_mfma(o[v], vf[n % PF], p1);
-          if (n + PF < 32) MLA_VREAD(sbv, n + PF, vf[n % PF]);
+          pv_mfma(o[v], vf[n % PFV], p1);
+          if (n + PFV < 32) MLA_VREAD(sbv, n + PFV, vf[n % PFV]);
           float arg = fmaf(sacc[v], c2, -m_run);
           if (kMask) arg = (8 * (v >> 2) + (v & 3) < lim) ? arg : -INFINITY;
           amax = fmaxf(amax, arg);
@@ -484,22 +512,24 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         }
         p0 = n0;
         p1 = n1;
+        // operands of the next weighted sum (stage k+1, already in LDS)
+#pragma unroll
+        for (int s = 0; s < PFV; ++s) MLA_VREAD(sbk, s, vf[s]);
       };
       for (int k = 0; k + 2 < nst; ++k) iteration(k, BoolC<false>{});
       if (nst >= 2) iteration(nst - 2, BoolC<true>{});
       {
         // weighted sum of the last stage
         const char LDS_AS* sbv = lds + ((nst - 1) % NS) * kStageBytes;
-        bf16x8 vf[PF];
-#pragma unroll
-        for (int s = 0; s < PF; ++s) MLA_VREAD(sbv, s, vf[s]);
 #pragma unroll
         for (int s = 0; s < 32; ++s) {
-          pv_mfma(o[s & 15], vf[s % PF], (s >> 4) ? p1 : p0);
-          if (s + PF < 32) MLA_VREAD(sbv, s + PF, vf[s % PF]);
+          pv_mfma(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
+          if (s + PFV < 32) MLA_VREAD(sbv, s + PFV, vf[s % PFV]);
         }
       }
-      // All waves are done reading the ring before it is refilled.
+      // Copies issued past the item's end are drained and all waves are done
+      // reading the ring before it is refilled.
+      wait_vmcnt_lgkm0<0>();
       block_barrier();
       if (!__syncthreads_or(amax > kRefHeadroom)) break;
       // Redo the item from its first stage with the head's largest score as
@@ -638,19 +668,43 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       const float w0 = e0 * inv, w1 = e1 * inv;
       const bool own_first = s0 == it;
       const __amdgpu_buffer_rsrc_t pr = part_rsrc(own_first ? s1 : s0);
+      // The partner's partial (64 blocks of 1 KB per wave) comes in through
+      // this wave's 36 KB of the LDS ring, free now, with direct-to-LDS loads
+      // in two rounds: every load of a round is in flight at once, and the
+      // blocks land in LDS in the layout they were stored in.
+      char LDS_AS* mb = lds + w * kStageBytes;
+      constexpr int kRound = kStageBytes / 1024;  // 36 blocks
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb)
+      for (int r0 = 0; r0 < 64; r0 += kRound) {
+        const int n = (64 - r0) < kRound ? (64 - r0) : kRound;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
-          float v[4];
+        for (int j = 0; j < kRound; ++j)
+          if (j < n) dma16_buffer(pr, uint32_t(r0 + j) * 1024 + lane_off, mb + j * 1024);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // LDS reads are not moved above earlier buffer stores either: read a
+        // group of blocks, then combine and store them.
+        constexpr int kGroup = 6;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float own = o[cb][4 * g + r] * own_inv;
-            v[r] = own_first ? fmaf(w1, x[r], w0 * own) : fmaf(w1, own, w0 * x[r]);
+        for (int j0 = 0; j0 < kRound; j0 += kGroup) {
+          f32x4 xs[kGroup];
+#pragma unroll
+          for (int jj = 0; jj < kGroup; ++jj)
+            if (j0 + jj < n) xs[jj] = *(const f32x4 LDS_AS*)(mb + (j0 + jj) * 1024 + lane_off);
+#pragma unroll
+          for (int jj = 0; jj < kGroup; ++jj) {
+            if (j0 + jj < n) {
+              const int blk = r0 + j0 + jj, cb = blk >> 2, g = blk & 3;
+              float v[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float own = o[cb][4 * g + r] * own_inv;
+                v[r] = own_first ? fmaf(w1, xs[jj][r], w0 * own) : fmaf(w1, own, w0 * xs[jj][r]);
+              }
+              if (head_ok) store_out4(cb, g, v);
+            }
           }
-          if (head_ok) store_out4(cb, g, v);
         }
+      }
       if (head_ok && hi_e == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, head_e * 4, 0, 0);
       continue;
