@@ -105,12 +105,15 @@ mla_status mla_decode(const void* q, const void* latent_cache,
  * Workspace layout written by the plan (int32 words unless noted):
  *   [0] number of work items   [1] chunk tokens   [2] data-check bits
  *   [3] work-queue counter (0 after the plan and after every attend call)
- *   [4] number of full items
+ *   [4] number of full items   [5] number of merge units (16 per request
+ *   split into 3 or more items)   [6] merge-unit queue counter (0 between
+ *   calls)
  *   at byte 256: per request 4 words (first full item, full-item count,
  *   remainder item or -1, total item count); then, 256-byte aligned, two
  *   counters per request (tickets taken, partials published; 0 between
- *   calls); then per item 4 words (request, first token, end token, the
- *   request's item count). */
+ *   calls); then the list of requests split into 3 or more items; then per
+ *   item 4 words (request, first token, end token, the request's item
+ *   count). */
 mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
                            int32_t M, int32_t BS, int32_t chunk_tokens,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -118,11 +121,13 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
 /* Step 2 — attention over every work item of the plan (the hot kernel), and
  * the split-KV merge.  An item that covers a whole request writes out/lse
  * directly; an empty request gets out = 0, lse = -inf.  When a request is
- * split, its items take tickets as they finish: every item but the last
- * writes its normalised fp32 output and log-sum-exp into the workspace, and
- * the last merges them with its own, summing in item order:
+ * split, its items write their normalised fp32 outputs and log-sum-exps into
+ * the workspace and they are merged, summing in item order:
  * lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s (bf16, RNE).
- * The result does not depend on which item finishes last.
+ * A request split in two is merged by whichever of its items finishes last
+ * (that item does not write its own partial); wider splits are merged in 16
+ * column blocks by whichever workgroups are free once every item has been
+ * taken.  The result does not depend on which workgroup merges or when.
  * Needs a plan made with the same B, H, M, BS. */
 mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              const int32_t* block_table, float scale,

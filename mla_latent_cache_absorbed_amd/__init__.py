@@ -61,8 +61,9 @@ class Workspace:
         return self.buf.data_ptr()
 
     def header(self) -> list:
-        """First words of the plan header: [n_items, chunk, check bits, queue, n_full]."""
-        return self.buf[:20].view(torch.int32).tolist()
+        """First words of the plan header: [n_items, chunk, check bits, item queue,
+        n_full, n_merge_units, merge-unit queue]."""
+        return self.buf[:28].view(torch.int32).tolist()
 
     def check_flags(self) -> int:
         return _lib.mla_decode_read_error(self.ptr, _stream())

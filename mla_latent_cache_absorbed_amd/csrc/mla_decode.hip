@@ -49,6 +49,7 @@ constexpr int kHdrBytes = 256;
 constexpr float kRefHeadroom = 64.0f;     // log2 units: P <= 2^64 before an item is redone
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kSc1 = 16;                  // cache-policy bit: agent-coherent access
+constexpr int kMergeMinItems = 3;         // splits this wide are merged by merge units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -64,7 +65,7 @@ __host__ __device__ inline int heads_padded(int H) { return H > 64 ? 128 : H > 3
 
 // Workspace sections (byte offsets).
 struct WsLayout {
-  size_t req_off, ctr_off, item_off, plse_off, po_off, total;
+  size_t req_off, ctr_off, big_off, item_off, plse_off, po_off, total;
   int cap;
 };
 
@@ -76,7 +77,8 @@ __host__ __device__ inline WsLayout ws_layout(int B, int H) {
   w.cap = B + kMaxExtraItems;
   w.req_off = kHdrBytes;
   w.ctr_off = align256(w.req_off + size_t(B) * 16);
-  w.item_off = align256(w.ctr_off + size_t(B) * 8);
+  w.big_off = align256(w.ctr_off + size_t(B) * 8);
+  w.item_off = align256(w.big_off + size_t(B) * 4);
   w.plse_off = align256(w.item_off + size_t(w.cap) * 16);
   w.po_off = align256(w.plse_off + size_t(w.cap) * hp * 4);
   w.total = align256(w.po_off + size_t(w.cap) * hp * kDV * 4);
@@ -155,6 +157,7 @@ struct AttendArgs {
   int32_t* hdr;          // workspace header (n_items, chunk, check bits, queue)
   const int4* req;       // per request: first full item, full count, remainder item, count
   int32_t* ctr;          // per request: [tickets taken, partials published] (0 between calls)
+  const int32_t* big;    // requests whose split is merged by merge units
   const int4* items;     // per item: request, first token, end token, request's item count
   float* part_lse;       // [cap, Hp]  log2-domain log-sum-exp of each split item
   float* part_o;         // [cap, Hp * 512] normalised output of each split item, in the
@@ -173,17 +176,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* cache, 
 // Direct-to-LDS loads, written out: the LDS address goes in M0 and each lane's
 // 16 bytes land at M0 + 16 * lane.  The compiler does not model these as LDS
 // writes, so it adds no waits of its own before later LDS reads; the stage
-// pipeline waits for them explicitly (vmcnt counts them in issue order).
-// One wait state after the M0 write precedes each load.
+// pipeline waits for them explicitly (vmcnt counts them in issue order), and
+// the waits and barriers that order them against LDS reads carry memory
+// clobbers.  Nor does the compiler see the asm's scalar operands, so the
+// hazards before a vector memory instruction are covered here: five wait
+// states, for a buffer resource or M0 just written by a VALU instruction
+// (the compiler reloads spilled SGPRs with v_readlane), which also covers the
+// one needed after an SALU write of M0.
 __device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                              const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(r), "{m0}"(m0));
 }
 __device__ __forceinline__ void dma16_global(const char* src, const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "{m0}"(m0));
 }
 
@@ -249,6 +257,7 @@ struct BoolC {
 };
 
 constexpr int kMergeSpinLimit = 1 << 22;  // polls for the partners of a split merge
+constexpr int kWaveBytesM = 32 * kDV * 4;  // one wave's share of an item's partial
 
 template <int NW, int NS>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
@@ -469,6 +478,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         char LDS_AS* sdst = lds + ((k + NS - 1) % NS) * kStageBytes;
         nxt = stage_ids(a, b, stage_base(k + NS), t1, bad);
         const char LDS_AS* sbk = lds + ((k + 1) % NS) * kStageBytes;
+        // With four waves each issues 9 loads per stage, spread between the
+        // score MFMAs; a lone or paired wave issues its 36 or 18 in a burst
+        // (spread that thin, every stall of the memory pipeline would land
+        // on an MFMA).
+        constexpr bool kSpread = NW == 4;
+        if (!kSpread)
+#pragma unroll
+          for (int j = 0; j < LPW; ++j) issue_load<NW>(a, cur, sdst, t1, w, lane16, j);
         bf16x8 kf[PFK];
 #pragma unroll
         for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sbk, s);
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
           else qk_mfma(sacc, kf[s % PFK], qreg[s]);
           if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sbk, s + PFK);
-          if (s % kDmaEvery == 0) issue_load<NW>(a, cur, sdst, t1, w, lane16, s / kDmaEvery);
+          if (kSpread && s % kDmaEvery == 0) issue_load<NW>(a, cur, sdst, t1, w, lane16, s / kDmaEvery);
           if ((s & 1) && (s >> 1) + 2 < 16) {
             const int n = (s >> 1) + 2;
             pv_mfma(o[n], vf[n % PFV], p0);
@@ -589,17 +606,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       continue;
     }
 
-    // Split request.  The item takes its ticket first: all but the last item
-    // of the request publish their normalised partial and wait no further;
-    // the last waits until they have all published and merges.  Partials are
-    // stored in the waves' accumulator layout (each store instruction writes
-    // 1 KB contiguous; the merging wave reads back the same lanes' values),
-    // with agent-coherent (sc1) accesses, so items on different XCDs exchange
-    // them without writing back or invalidating whole L2 caches.
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&a.ctr[2 * b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    // Split request.  Partials are stored in the waves' accumulator layout
+    // (each store instruction writes 1 KB contiguous; a merging wave reads
+    // back the same lanes' values), with agent-coherent (sc1) accesses, so
+    // items on different XCDs exchange them without writing back or
+    // invalidating whole L2 caches.  A request split in two is merged by its
+    // last item; wider splits by merge units once the item queue is empty.
     constexpr int kWaveBytes = 32 * kDV * 4;  // one wave's share of a partial
     auto part_rsrc = [&](int slot) {
       return __builtin_amdgcn_make_buffer_rsrc(
@@ -608,7 +620,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
     const uint32_t lane_off = uint32_t(lane_e) * 16;
-    if (ticket != cnt - 1) {
+    auto publish = [&]() {
       const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb)
@@ -625,15 +637,28 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       __syncthreads();
       if (threadIdx.x == 0)
         __hip_atomic_fetch_add(&a.ctr[2 * b + 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (cnt >= kMergeMinItems) {
+      publish();
       continue;
     }
-    // The last item: its partners all took their tickets earlier, so they
-    // are past their stage loops and only have stores left; the wait ends.
-    // It is bounded all the same, and a flag is raised if the bound is hit.
+    // Two items: the item takes its ticket first; the first publishes and
+    // waits no further, the last waits until its partner has published and
+    // merges.
+    if (threadIdx.x == 0)
+      s_ticket = __hip_atomic_fetch_add(&a.ctr[2 * b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    if (ticket == 0) {
+      publish();
+      continue;
+    }
+    // The partner took its ticket earlier, so it is past its stage loop and
+    // only has stores left; the wait ends.  It is bounded all the same, and
+    // a flag is raised if the bound is hit.
     if (threadIdx.x == 0) {
       for (int spin = 0;; ++spin) {
-        if (__hip_atomic_load(&a.ctr[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cnt - 1)
-          break;
+        if (__hip_atomic_load(&a.ctr[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= 1) break;
         if (spin >= kMergeSpinLimit) {
           atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
           break;
@@ -645,20 +670,19 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    // log-sum-exp merge (log2 domain): lse = log2 sum_s 2^lse_s,
-    // out = sum_s 2^(lse_s - lse) o_s, with o_s the normalised partials.
-    // Terms are summed in item order (out = fma(w_s, o_s, acc) from acc = 0),
-    // and this item's own term is the very value it would have published, so
-    // the result does not depend on which item finished last.
-    const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
-    auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
-    auto lse_of = [&](int slot) {
-      return slot == it ? lse2
-                        : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                              plse_r, uint32_t(slot * HP + head_e) * 4, 0, kSc1));
-    };
-    if (cnt == 2) {
-      // the common split: one partner, whose loads are all independent
+    {
+      // log-sum-exp merge (log2 domain): lse = log2 sum_s 2^lse_s,
+      // out = sum_s 2^(lse_s - lse) o_s, with o_s the normalised partials.
+      // Terms are summed in item order, and this item's own term is the very
+      // value it would have published, so the result does not depend on
+      // which item finished last.
+      const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
+      auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
+      auto lse_of = [&](int slot) {
+        return slot == it ? lse2
+                          : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                plse_r, uint32_t(slot * HP + head_e) * 4, 0, kSc1));
+      };
       const int s0 = slot_of(0), s1 = slot_of(1);
       const float l0 = lse_of(s0), l1 = lse_of(s1);
       const float mlse = fmaxf(l0, l1);
@@ -707,13 +731,63 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       }
       if (head_ok && hi_e == 0)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, head_e * 4, 0, 0);
-      continue;
     }
-    // General split: per-item weights of this wave's heads go to the LDS
-    // ring (free now), 32 floats per item, for up to kSlotsLds items.
-    constexpr int kSlotsLds = NS * kStageBytes / (NW * 32 * 4);
-    float LDS_AS* wsl = (float LDS_AS*)(lds) + w * 32 * kSlotsLds + hl_e;
-    const bool in_lds = cnt <= kSlotsLds;
+  }
+
+  // ---- merge units ----
+  // Requests split into kMergeMinItems or more items are merged after the
+  // item queue is empty, by every workgroup: a request has 4 NW units, unit
+  // u covering the 512 / (4 NW) columns starting at kCb * 32 * (u % (4 NW))
+  // of request big[u / (4 NW)], for all heads (one 32-head block per wave).
+  // Every item of those requests has been taken from the queue, so each is
+  // running or done and the wait for their partials ends; it is bounded all
+  // the same.  Terms are summed in item order from the published values, so
+  // the result does not depend on which workgroup merges or when.
+  constexpr int kUnits = 4 * NW;      // units per request
+  constexpr int kCb = 16 / kUnits;    // 32-column blocks per unit
+  const int n_units = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[5]);
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[6], 1);
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();
+    if (u >= n_units) {
+      if (threadIdx.x == 0 && u == n_units + int(gridDim.x) - 1) atomicExch(&a.hdr[6], 0);
+      break;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.big)[u / kUnits]);
+    const int cb0 = (u % kUnits) * kCb;
+    const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
+    const int cnt = __builtin_amdgcn_readfirstlane(rq[3]);
+    if (threadIdx.x == 0) {
+      for (int spin = 0;; ++spin) {
+        if (__hip_atomic_load(&a.ctr[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cnt) break;
+        if (spin >= kMergeSpinLimit) {
+          atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    int lane_m = lane;
+    asm volatile("" : "+v"(lane_m));
+    const int head_m = w * 32 + (lane_m & 31);
+    const int hi_m = lane_m >> 5;
+    const bool ok_m = head_m < a.H;
+    const uint32_t moff = uint32_t(lane_m) * 16 + uint32_t(cb0) * 4096;
+    auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
+    const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
+    auto lse_of = [&](int slot) {
+      return __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(plse_r, uint32_t(slot * HP + head_m) * 4, 0, kSc1));
+    };
+    // per-item log-sum-exps of this lane's head, then the weights, staged in
+    // the LDS ring (free now) for up to kSlots items
+    constexpr int kSlots = NS * kStageBytes / (NW * 32 * 4);
+    float LDS_AS* wsl = (float LDS_AS*)(lds) + w * 32 * kSlots + (lane_m & 31);
+    const bool in_lds = cnt <= kSlots;
     float mlse = -INFINITY;
     for (int s = 0; s < cnt; ++s) {
       const float l = lse_of(slot_of(s));
@@ -730,35 +804,506 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     auto weight = [&](int s) {
       return (in_lds ? wsl[32 * s] : __builtin_amdgcn_exp2f(lse_of(slot_of(s)) - mlse)) * inv;
     };
+    // 4 kCb KB of each item per wave, 32 loads in flight at a time
+    constexpr int kNB = 4 * kCb;           // 1 KB blocks per item
+    constexpr int kBatch = 32 / kNB;       // items per batch of loads
+    f32x4 acc[kNB] = {};
+    for (int s0 = 0; s0 < cnt; s0 += kBatch) {
+      f32x4 x[kBatch][kNB];
+      float wt[kBatch];
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
-      f32x16 acc = {};
-      for (int s = 0; s < cnt; ++s) {
-        const int slot = slot_of(s);
-        const float ws = weight(s);
-        const __amdgpu_buffer_rsrc_t pr = part_rsrc(slot);
+      for (int j = 0; j < kBatch; ++j) {
+        if (s0 + j < cnt) {
+          const int slot = slot_of(s0 + j);
+          const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(a.part_o + (size_t(slot) * HP + w * 32) * kDV), (short)0, kWaveBytesM, 0x00020000);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v4;
-          if (slot == it) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
-          } else {
-            v4 = __builtin_amdgcn_raw_buffer_load_b128(pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[4 * g + r] = fmaf(ws, v4[r], acc[4 * g + r]);
+          for (int g = 0; g < kNB; ++g)
+            x[j][g] = __builtin_amdgcn_raw_buffer_load_b128(pr, moff + g * 1024, 0, kSc1);
+          wt[j] = weight(s0 + j);
         }
       }
-      if (head_ok)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-          store_out4(cb, g, v);
-        }
+      for (int j = 0; j < kBatch; ++j)
+        if (s0 + j < cnt)
+#pragma unroll
+          for (int g = 0; g < kNB; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(wt[j], x[j][g][r], acc[g][r]);
     }
-    if (head_ok && hi_e == 0)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, head_e * 4, 0, 0);
+    if (ok_m) {
+      const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
+      // block g = 4 c + gg holds columns 32 (cb0 + c) + 8 gg + 4 hi .. +3
+      const uint32_t ooff = uint32_t(head_m * kDV + 4 * hi_m + 32 * cb0) * 2;
+#pragma unroll
+      for (int g = 0; g < kNB; ++g) {
+        bf16x4 h4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h4[r] = (__bf16)acc[g][r];
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
+                                              ooff + (32 * (g >> 2) + 8 * (g & 3)) * 2, 0, 0);
+      }
+      if (cb0 == 0 && hi_m == 0) {
+        const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r,
+                                              head_m * 4, 0, 0);
+      }
+    }
+    // the request's last unit leaves its counters ready for the next call
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int t = __hip_atomic_fetch_add(&a.ctr[2 * b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == kUnits - 1) {
+        __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attend, narrow variant (H <= 32): independent wave workers
+//
+// With at most 32 heads each cached token carries at most 32 heads' worth of
+// MFMA work for its 1,152 bytes, far below the MFMA ridge: this shape is
+// bound by HBM.  So every wave of a workgroup is an independent worker with
+// its own 36 KB LDS slot: it takes items from the queue itself, loads a
+// stage, runs the 36 score MFMAs, the softmax and the 32 weighted-sum MFMAs,
+// and only then loads its next stage into the same slot.  The four waves of
+// a compute unit overlap one another's load latency (up to four stages in
+// flight per compute unit) and none ever waits for another.  Splits are
+// merged as in the wide kernel, by wave: a request split in two by its last
+// item, wider splits by merge units of 128 columns.
+// ---------------------------------------------------------------------------
+constexpr int kNarrowWaves = 4;
+constexpr int kNarrowUnits = 4;  // merge units per widely split request
+
+__global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNarrowWaves * kStageBytes];
+  constexpr int PFK = 4;  // score operand reads in flight
+  constexpr int PFV = 2;  // weighted-sum operand reads in flight
+  constexpr int HP = 32;  // heads of a partial
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char LDS_AS* slot = (char LDS_AS*)(lds_raw) + w * kStageBytes;
+  const int hl = lane & 31;
+  const int hi = lane >> 5;
+  const bool head_ok = hl < a.H;
+  const float c2 = a.scale_log2;
+  const int n_items = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[0]);
+  const int n_units = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[5]);
+  const int n_workers = int(gridDim.x) * kNarrowWaves;
+  const int xlane = (lane ^ 32) << 2;
+  auto pair_max = [&](float x) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_ds_bpermute(xlane, __float_as_int(x))));
+  };
+  auto pair_sum = [&](float x) {
+    return x + __int_as_float(__builtin_amdgcn_ds_bpermute(xlane, __float_as_int(x)));
+  };
+  // one atomic per wave, result broadcast from lane 0
+  auto wave_fetch_add = [&](int32_t* p) {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // lane 0 polls a counter until it reaches `target` (bounded)
+  auto wave_wait = [&](int32_t* p, int target) {
+    if (lane == 0) {
+      for (int spin = 0;; ++spin) {
+        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+        if (spin >= kMergeSpinLimit) {
+          atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  };
+
+  // operand read offsets, as in the wide kernel
+  int qk_off[8];
+  {
+    const int xa = swzA(hl);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qk_off[j] = hl * 1024 + ((((2 * j) | hi)) ^ xa) * 16;
+  }
+  const int qkb = kRegionB + hi * 512 + hl * 16;
+  int pv_off[2][4];
+  {
+    const int r = (lane >> 2) & 3;
+    const int cc = (((lane >> 4) & 1) << 1) | ((lane >> 1) & 1);
+    const int u0 = lane & 1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int T = 8 * e + 4 * hi + r;
+      const int sa = swzA(T);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv_off[e][j] = T * 1024 + (((4 * j) | cc) ^ sa) * 16 + 8 * u0;
+    }
+  }
+#define MLA_KREAD(sb, s)                                                               \
+  ((s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))      \
+            : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
+#define MLA_VREAD(sb, n, dst)                                                               \
+  do {                                                                                      \
+    const int cb_ = (n) & 15, kk_ = (n) >> 4;                                               \
+    const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                        \
+    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
+        (bf16x4 LDS_AS*)((sb) + pv_off[0][cb_ & 3] + imm_));                                \
+    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
+        (bf16x4 LDS_AS*)((sb) + pv_off[1][cb_ & 3] + imm_));                                \
+    dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
+  } while (0)
+
+  for (;;) {
+    const int it = wave_fetch_add(&a.hdr[3]);
+    if (it >= n_items) {
+      // every worker makes exactly one failing fetch; the last of them
+      // leaves the queue at 0 for the next call
+      if (lane == 0 && it == n_items + n_workers - 1) atomicExch(&a.hdr[3], 0);
+      break;
+    }
+    const i32x4 item = ((const CONST_AS i32x4*)a.items)[it];
+    const int b = __builtin_amdgcn_readfirstlane(item[0]);
+    const int t0 = __builtin_amdgcn_readfirstlane(item[1]);
+    const int t1 = __builtin_amdgcn_readfirstlane(item[2]);
+    const int cnt = __builtin_amdgcn_readfirstlane(item[3]);
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int hl_e = lane_e & 31;
+    const int hi_e = lane_e >> 5;
+    const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
+    const uint32_t out_off = uint32_t(hl_e * kDV + 4 * hi_e) * 2;
+    auto store_out4 = [&](int cb, int g, const float (&v)[4]) {
+      bf16x4 h4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h4[r] = (__bf16)v[r];
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
+                                            out_off + (32 * cb + 8 * g) * 2, 0, 0);
+    };
+    if (t1 <= t0) {
+      // a request with no cached tokens: out = 0, lse = -inf
+      if (head_ok) {
+        const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) store_out4(cb, g, z);
+        if (hi_e == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), lse_r, hl_e * 4, 0, 0);
+      }
+      continue;
+    }
+    const int nst = (t1 - t0 + kSub - 1) / kSub;
+    int bad = 0;
+    f32x16 o[16];
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+    float m_run = -INFINITY, amax = -INFINITY, la = 0.0f, lb = 0.0f;
+    uint32_t lane16 = uint32_t(lane) * 16;
+    asm volatile("" : "+v"(lane16));
+    for (;;) {
+      // fixed exponent reference from the item's first stage, with a redo if
+      // a later score exceeds it by more than the headroom (as in the wide
+      // kernel)
+      bf16x8 qreg[36];
+      {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            a.q + (size_t(b) * a.H + (head_ok ? hl : 0)) * kD + 8 * hi);
+#pragma unroll
+        for (int s = 0; s < 36; ++s) {
+          bf16x8 v = qp[2 * s];
+          if (!head_ok) v = bf16x8{};
+          qreg[s] = v;
+        }
+      }
+      for (int st = 0; st < nst; ++st) {
+        const StageIds id = stage_ids(a, b, t0 + st * kSub, t1, bad);
+        // this wave's reads of the slot are done before it is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 36; ++j) issue_load<1>(a, id, slot, t1, 0, lane16, j);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        f32x16 sacc;
+        {
+          bf16x8 kf[PFK];
+#pragma unroll
+          for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(slot, s);
+#pragma unroll
+          for (int s = 0; s < 36; ++s) {
+            if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
+            else qk_mfma(sacc, kf[s % PFK], qreg[s]);
+            if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(slot, s + PFK);
+          }
+          qk_drain(sacc);
+        }
+        bf16x8 p0, p1;
+        {
+          // register v holds token 4hi + 8(v/4) + (v%4) of the stage
+          const int lim = t1 - (t0 + st * kSub) - 4 * hi;
+          if (m_run == -INFINITY) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              if (8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, sacc[v] * c2);
+            m_run = pair_max(mx);
+          }
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float arg = (8 * (v >> 2) + (v & 3) < lim) ? fmaf(sacc[v], c2, -m_run) : -INFINITY;
+            amax = fmaxf(amax, arg);
+            const float pv = __builtin_amdgcn_exp2f(arg);
+            if (v & 1) lb += pv;
+            else la += pv;
+            if (v < 8) p0[v] = (__bf16)pv;
+            else p1[v - 8] = (__bf16)pv;
+          }
+        }
+        {
+          bf16x8 vf[PFV];
+#pragma unroll
+          for (int s = 0; s < PFV; ++s) MLA_VREAD(slot, s, vf[s]);
+#pragma unroll
+          for (int s = 0; s < 32; ++s) {
+            pv_mfma(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
+            if (s + PFV < 32) MLA_VREAD(slot, s + PFV, vf[s % PFV]);
+          }
+        }
+      }
+      if (__ballot(amax > kRefHeadroom) == 0) break;
+      m_run += pair_max(amax);
+      amax = -INFINITY;
+      la = 0.0f;
+      lb = 0.0f;
+      pv_drain(o);
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
+    }
+    pv_drain(o);
+    if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
+
+    const float l_tot = pair_sum(la + lb);
+    const float lse2 = m_run + log2f(l_tot);
+    const float own_inv = 1.0f / l_tot;
+    if (cnt == 1) {
+      if (head_ok) {
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * g + r] * own_inv;
+            store_out4(cb, g, v);
+          }
+        if (hi_e == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2), lse_r, hl_e * 4, 0, 0);
+      }
+      continue;
+    }
+    // split request: partial in the accumulator layout (lanes of padding
+    // heads store nothing)
+    auto part_rsrc = [&](int sl) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_o + size_t(sl) * HP * kDV), (short)0,
+                                               HP * kDV * 4, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
+    const uint32_t lane_off = uint32_t(lane_e) * 16;
+    auto publish = [&]() {
+      if (head_ok) {
+        const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
+            __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
+          }
+        if (hi_e == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r,
+                                                uint32_t(it * HP + hl_e) * 4, 0, kSc1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is out
+      if (lane == 0) __hip_atomic_fetch_add(&a.ctr[2 * b + 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (cnt >= kMergeMinItems) {
+      publish();
+      continue;
+    }
+    const int ticket = wave_fetch_add(&a.ctr[2 * b]);
+    if (ticket == 0) {
+      publish();
+      continue;
+    }
+    // the last of two: its partner took its ticket earlier and only has
+    // stores left
+    wave_wait(&a.ctr[2 * b + 1], 1);
+    if (lane == 0) {
+      __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    {
+      const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
+      auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
+      auto lse_of = [&](int sl) {
+        return sl == it ? lse2
+                        : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                              plse_r, uint32_t(sl * HP + hl_e) * 4, 0, kSc1));
+      };
+      const int s0 = slot_of(0), s1 = slot_of(1);
+      const float l0 = lse_of(s0), l1 = lse_of(s1);
+      const float mlse = fmaxf(l0, l1);
+      const float e0 = __builtin_amdgcn_exp2f(l0 - mlse), e1 = __builtin_amdgcn_exp2f(l1 - mlse);
+      const float lam = e0 + e1;
+      const float inv = 1.0f / lam;
+      const float w0 = e0 * inv, w1 = e1 * inv;
+      const bool own_first = s0 == it;
+      const __amdgpu_buffer_rsrc_t pr = part_rsrc(own_first ? s1 : s0);
+      // the partner's partial through this wave's slot, in two rounds
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      constexpr int kRound = kStageBytes / 1024;  // 36 blocks
+#pragma unroll
+      for (int r0 = 0; r0 < 64; r0 += kRound) {
+        const int n = (64 - r0) < kRound ? (64 - r0) : kRound;
+#pragma unroll
+        for (int j = 0; j < kRound; ++j)
+          if (j < n) dma16_buffer(pr, uint32_t(r0 + j) * 1024 + lane_off, slot + j * 1024);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        constexpr int kGroup = 6;
+#pragma unroll
+        for (int j0 = 0; j0 < kRound; j0 += kGroup) {
+          f32x4 xs[kGroup];
+#pragma unroll
+          for (int jj = 0; jj < kGroup; ++jj)
+            if (j0 + jj < n) xs[jj] = *(const f32x4 LDS_AS*)(slot + (j0 + jj) * 1024 + lane_off);
+#pragma unroll
+          for (int jj = 0; jj < kGroup; ++jj) {
+            if (j0 + jj < n) {
+              const int blk = r0 + j0 + jj, cb = blk >> 2, g = blk & 3;
+              float v[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float own = o[cb][4 * g + r] * own_inv;
+                v[r] = own_first ? fmaf(w1, xs[jj][r], w0 * own) : fmaf(w1, own, w0 * xs[jj][r]);
+              }
+              if (head_ok) store_out4(cb, g, v);
+            }
+          }
+        }
+        // this round's reads are done before the next round refills the slot
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      if (head_ok && hi_e == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, hl_e * 4, 0, 0);
+    }
+  }
+#undef MLA_KREAD
+#undef MLA_VREAD
+
+  // ---- merge units: 128 columns (16 blocks of 1 KB per item) each ----
+  for (;;) {
+    const int u = wave_fetch_add(&a.hdr[6]);
+    if (u >= n_units) {
+      if (lane == 0 && u == n_units + n_workers - 1) atomicExch(&a.hdr[6], 0);
+      break;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.big)[u / kNarrowUnits]);
+    const int cb0 = (u % kNarrowUnits) * (16 / kNarrowUnits);
+    const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
+    const int cnt = __builtin_amdgcn_readfirstlane(rq[3]);
+    wave_wait(&a.ctr[2 * b + 1], cnt);
+    int lane_m = lane;
+    asm volatile("" : "+v"(lane_m));
+    const int hl_m = lane_m & 31;
+    const int hi_m = lane_m >> 5;
+    const bool ok_m = hl_m < a.H;
+    const uint32_t moff = uint32_t(lane_m) * 16 + uint32_t(cb0) * 4096;
+    auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
+    const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
+    auto lse_of = [&](int sl) {
+      return __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(plse_r, uint32_t(sl * HP + hl_m) * 4, 0, kSc1));
+    };
+    // weights of this lane's head in this wave's slot (the slot's previous
+    // reads are done), up to kSlots items
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int kSlots = kStageBytes / (32 * 4);
+    float LDS_AS* wsl = (float LDS_AS*)(slot) + hl_m;
+    const bool in_lds = cnt <= kSlots;
+    float mlse = -INFINITY;
+    for (int s = 0; s < cnt; ++s) {
+      const float l = lse_of(slot_of(s));
+      mlse = fmaxf(mlse, l);
+      if (in_lds) wsl[32 * s] = l;
+    }
+    float lam = 0.0f;
+    for (int s = 0; s < cnt; ++s) {
+      const float e = __builtin_amdgcn_exp2f((in_lds ? wsl[32 * s] : lse_of(slot_of(s))) - mlse);
+      lam += e;
+      if (in_lds) wsl[32 * s] = e;
+    }
+    const float inv = 1.0f / lam;
+    auto weight = [&](int s) {
+      return (in_lds ? wsl[32 * s] : __builtin_amdgcn_exp2f(lse_of(slot_of(s)) - mlse)) * inv;
+    };
+    constexpr int kNB = 4 * (16 / kNarrowUnits);  // 1 KB blocks per item
+    constexpr int kBatch = 32 / kNB;
+    f32x4 acc[kNB] = {};
+    for (int s0 = 0; s0 < cnt; s0 += kBatch) {
+      f32x4 x[kBatch][kNB];
+      float wt[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (s0 + j < cnt) {
+          const int sl = slot_of(s0 + j);
+          const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(a.part_o + size_t(sl) * HP * kDV), (short)0, HP * kDV * 4, 0x00020000);
+#pragma unroll
+          for (int g = 0; g < kNB; ++g)
+            x[j][g] = __builtin_amdgcn_raw_buffer_load_b128(pr, moff + g * 1024, 0, kSc1);
+          wt[j] = weight(s0 + j);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (s0 + j < cnt)
+#pragma unroll
+          for (int g = 0; g < kNB; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(wt[j], x[j][g][r], acc[g][r]);
+    }
+    if (ok_m) {
+      const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
+      const uint32_t ooff = uint32_t(hl_m * kDV + 4 * hi_m + 32 * cb0) * 2;
+#pragma unroll
+      for (int g = 0; g < kNB; ++g) {
+        bf16x4 h4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h4[r] = (__bf16)acc[g][r];
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
+                                              ooff + (32 * (g >> 2) + 8 * (g & 3)) * 2, 0, 0);
+      }
+      if (cb0 == 0 && hi_m == 0) {
+        const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r,
+                                              hl_m * 4, 0, 0);
+      }
+    }
+    // the request's last unit leaves its counters ready for the next call
+    const int t = wave_fetch_add(&a.ctr[2 * b]);
+    if (lane == 0 && t == kNarrowUnits - 1) {
+      __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -796,8 +1341,8 @@ __device__ __forceinline__ int2 block_scan(int v, int* s_scan) {
 // request, then one item per empty request.
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
-    int ovh, int cap, int32_t* __restrict__ hdr, int4* __restrict__ req, int32_t* __restrict__ ctr,
-    int4* __restrict__ items) {
+    int ovh, int cap, int units_per_req, int32_t* __restrict__ hdr, int4* __restrict__ req,
+    int32_t* __restrict__ ctr, int32_t* __restrict__ big, int4* __restrict__ items) {
   __shared__ long long s_cost[kPlanThreads];
   __shared__ int s_chunk[kPlanThreads];
   __shared__ int s_scan[kPlanThreads];
@@ -855,29 +1400,34 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   const int NE = block_scan(ne_loc, s_scan).y;
   const int any_bad = block_scan(bad, s_scan).y;
 
-  // 3) per-request placement from exclusive scans
-  int carry_f = 0, carry_r = 0, carry_e = 0;
+  // 3) per-request placement from exclusive scans; requests split into
+  //    kMergeMinItems or more items are listed for the merge units
+  int carry_f = 0, carry_r = 0, carry_e = 0, carry_b = 0;
   for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
     const int b = b0 + tid;
     const int L = (b < B) ? min(max(seq_lens[b], 0), Lmax) : 0;
     const int nf = L / chunk;
     const int nr = (L % chunk) ? 1 : 0;
     const int ne = (b < B && L == 0) ? 1 : 0;
+    const int cnt = nf + nr;
+    const int nbg = (b < B && cnt >= kMergeMinItems) ? 1 : 0;
     const int2 fs = block_scan(nf, s_scan);
     const int2 rs = block_scan(nr, s_scan);
     const int2 es = block_scan(ne, s_scan);
+    const int2 bs = block_scan(nbg, s_scan);
     if (b < B) {
       const int fbeg = carry_f + fs.x - nf;
-      const int cnt = nf + nr;
       const int ritem = nr ? (NF + carry_r + rs.x - nr) : -1;
       req[b] = make_int4(fbeg, nf, ritem, cnt);
       for (int s = 0; s < nf; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
       if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt);
       if (ne) items[NF + NR + carry_e + es.x - 1] = make_int4(b, 0, 0, 0);
+      if (nbg) big[carry_b + bs.x - 1] = b;
     }
     carry_f += fs.y;
     carry_r += rs.y;
     carry_e += es.y;
+    carry_b += bs.y;
   }
 
   // 4) header
@@ -887,6 +1437,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     hdr[2] = any_bad ? MLA_CHECK_SEQ_LEN_RANGE : 0;
     hdr[3] = 0;
     hdr[4] = NF;
+    hdr[5] = carry_b * units_per_req;
+    hdr[6] = 0;
   }
 }
 
@@ -938,13 +1490,16 @@ mla_status check_workspace(const void* ws, size_t ws_bytes, int B, int H) {
 }
 
 // Kernel variant for H heads: waves per workgroup, LDS stages, workgroups per CU.
+// Kernel variant for H heads: waves per workgroup (0: the narrow kernel of
+// independent wave workers), queue workers per compute unit, merge units per
+// widely split request.
 struct Variant {
-  int nw, ns, wgs_per_cu;
+  int nw, workers_per_cu, units_per_req;
 };
 Variant pick_variant(int H) {
-  if (H > 64) return {4, 4, 1};
-  if (H > 32) return {2, 4, 1};
-  return {1, 3, 1};
+  if (H > 64) return {4, 1, 16};
+  if (H > 32) return {2, 1, 8};
+  return {0, kNarrowWaves, kNarrowUnits};
 }
 
 int item_overhead_tokens(int H) { return 32 + 2 * H; }
@@ -1008,10 +1563,11 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_
   const Variant v = pick_variant(H);
   char* ws = static_cast<char*>(workspace);
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
-                     seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.wgs_per_cu,
-                     (int)chunk_tokens, item_overhead_tokens(H), L.cap,
+                     seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.workers_per_cu,
+                     (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req,
                      reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
                      reinterpret_cast<int32_t*>(ws + L.ctr_off),
+                     reinterpret_cast<int32_t*>(ws + L.big_off),
                      reinterpret_cast<int4*>(ws + L.item_off));
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -1037,6 +1593,7 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
   a.req = reinterpret_cast<const int4*>(ws + L.req_off);
   a.ctr = reinterpret_cast<int32_t*>(ws + L.ctr_off);
   a.items = reinterpret_cast<const int4*>(ws + L.item_off);
+  a.big = reinterpret_cast<const int32_t*>(ws + L.big_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
   a.part_o = reinterpret_cast<float*>(ws + L.po_off);
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -1046,13 +1603,16 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
   a.M = M;
   a.lgBS = ilog2_exact(BS);
   const Variant v = pick_variant(H);
-  const int grid = ncu * v.wgs_per_cu;
+  const int grid = ncu;  // one workgroup per compute unit
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   switch (v.nw) {
     case 4: e = launch_attend<4, 4>(a, grid, st); break;
     case 2: e = launch_attend<2, 4>(a, grid, st); break;
-    default: e = launch_attend<1, 3>(a, grid, st); break;
+    default:
+      hipLaunchKernelGGL(mla_attend_narrow_kernel, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
+      e = hipGetLastError();
+      break;
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

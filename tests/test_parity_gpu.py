@@ -89,13 +89,27 @@ def test_block_sizes(BS):
     _assert_parity(out, lse, ro, rl, f"BS={BS}")
 
 
-@pytest.mark.parametrize("chunk", [32, 64, 96, 256, 1024])
-def test_forced_splits(chunk):
+@pytest.mark.parametrize("H,chunk", [(128, 32), (128, 64), (128, 96), (128, 256), (128, 1024),
+                                     (48, 32), (48, 1024), (16, 32), (16, 96), (16, 1024)])
+def test_forced_splits(H, chunk):
+    """Splits of two items (merged by the last item) and of many (merge units),
+    for the four-wave, two-wave and narrow (independent wave) kernels."""
     lens = [1, 40, 333, 1024, 2500]
-    w = _to_gpu(wl.make_custom(lens, H=128, BS=16, seed=7, poison_unused=True))
-    out, lse = _run(w, chunk_tokens=chunk)
+    w = _to_gpu(wl.make_custom(lens, H=H, BS=16, seed=7, poison_unused=True))
+    ws = mla.Workspace(w.B, w.H, w.M, w.BS)
+    out, lse = _run(w, chunk_tokens=chunk, ws=ws)
     ro, rl = _oracle(w)
-    _assert_parity(out, lse, ro, rl, f"chunk={chunk}")
+    _assert_parity(out, lse, ro, rl, f"H={H} chunk={chunk}")
+    hdr = ws.header()
+    # queues back at 0, no data-check or merge-wait flag raised
+    assert hdr[3] == 0 and hdr[6] == 0 and ws.check_flags() == 0, hdr
+    # the same plan serves a second call with identical results
+    out2 = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse2 = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    mla.attend(w.q, w.cache, w.block_table, w.scale, out2, lse2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.float().cpu().numpy(), out)
+    assert np.array_equal(lse2.cpu().numpy(), lse)
 
 
 def test_empty_requests_and_empty_batch():
@@ -229,8 +243,10 @@ def test_full_size_sampled(name, reqs):
     mla.decode(w.q, w.cache, w.block_table, w.seq_lens, w.scale, out, lse, workspace=ws)
     torch.cuda.synchronize()
     hdr = ws.header()
-    _say(f"[full-size] {name}: plan items={hdr[0]} chunk={hdr[1]} flags={hdr[2]}")
-    assert hdr[2] == 0
+    _say(f"[full-size] {name}: plan items={hdr[0]} chunk={hdr[1]} flags={hdr[2]} "
+         f"merge units={hdr[5]}")
+    assert hdr[2] == 0 and hdr[3] == 0 and hdr[6] == 0
+    assert ws.check_flags() == 0
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
     assert np.isfinite(o).all() and np.isfinite(l).all()
