@@ -316,17 +316,29 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     }
   }
 
+  // Workgroup g takes item g directly; items grid, grid+1, ... come from the
+  // queue.  With no more items than workgroups no atomic is needed at all.
+  // Otherwise every workgroup makes exactly one failing fetch, and the last
+  // fetch of all (it returns n_items - 1) leaves the queue at 0 so that the
+  // same plan serves the next call.
+  const int grid = int(gridDim.x);
+  bool first = true;
   for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[3], 1);
-    __syncthreads();
-    const int it = __builtin_amdgcn_readfirstlane(s_item);
-    __syncthreads();
-    if (it >= n_items) {
-      // Every workgroup makes exactly one failing fetch; the last of them
-      // leaves the queue at 0 so that the same plan serves the next call.
-      if (threadIdx.x == 0 && it == n_items + int(gridDim.x) - 1) atomicExch(&a.hdr[3], 0);
-      break;
+    int it = int(blockIdx.x);
+    if (!first) {
+      if (n_items <= grid) break;
+      if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[3], 1);
+      __syncthreads();
+      const int v = __builtin_amdgcn_readfirstlane(s_item);
+      __syncthreads();
+      if (v + grid >= n_items) {
+        if (threadIdx.x == 0 && v == n_items - 1) atomicExch(&a.hdr[3], 0);
+        break;
+      }
+      it = v + grid;
     }
+    first = false;
+    if (it >= n_items) continue;
 
     const i32x4 item = ((const CONST_AS i32x4*)a.items)[it];
     const int b = __builtin_amdgcn_readfirstlane(item[0]);
@@ -747,6 +759,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   constexpr int kCb = 16 / kUnits;    // 32-column blocks per unit
   const int n_units = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[5]);
   for (;;) {
+    if (n_units == 0) break;
     if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[6], 1);
     __syncthreads();
     const int u = __builtin_amdgcn_readfirstlane(s_item);
@@ -957,14 +970,23 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
   } while (0)
 
+  // worker k takes item k directly, later items from the queue (as in the
+  // wide kernel, by wave)
+  const int worker = int(blockIdx.x) * kNarrowWaves + w;
+  bool first = true;
   for (;;) {
-    const int it = wave_fetch_add(&a.hdr[3]);
-    if (it >= n_items) {
-      // every worker makes exactly one failing fetch; the last of them
-      // leaves the queue at 0 for the next call
-      if (lane == 0 && it == n_items + n_workers - 1) atomicExch(&a.hdr[3], 0);
-      break;
+    int it = worker;
+    if (!first) {
+      if (n_items <= n_workers) break;
+      const int v = wave_fetch_add(&a.hdr[3]);
+      if (v + n_workers >= n_items) {
+        if (lane == 0 && v == n_items - 1) atomicExch(&a.hdr[3], 0);
+        break;
+      }
+      it = v + n_workers;
     }
+    first = false;
+    if (it >= n_items) continue;
     const i32x4 item = ((const CONST_AS i32x4*)a.items)[it];
     const int b = __builtin_amdgcn_readfirstlane(item[0]);
     const int t0 = __builtin_amdgcn_readfirstlane(item[1]);
@@ -1208,6 +1230,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 
   // ---- merge units: 128 columns (16 blocks of 1 KB per item) each ----
   for (;;) {
+    if (n_units == 0) break;
     const int u = wave_fetch_add(&a.hdr[6]);
     if (u >= n_units) {
       if (lane == 0 && u == n_units + n_workers - 1) atomicExch(&a.hdr[6], 0);
