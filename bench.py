@@ -66,8 +66,11 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
-def hbm_traffic_record():
-    """Counter-measured HBM bytes per attend launch, if taken on this source."""
+def hbm_traffic_record(name: str):
+    """Counter-measured HBM bytes per attend launch, if taken on this source
+    and this workload."""
+    if name != "dp_rank":
+        return None
     try:
         rec = json.load(open(COUNTERS))
     except (OSError, ValueError):
@@ -217,12 +220,12 @@ def main():
         "roofline_frac_step": roof_t * layers / (ms_step * 1e-3),
         "roofline": {
             "bound": bound,
-            "kernel": "mla_attend_kernel",
+            "kernel": "mla_attend_narrow_kernel" if H <= 32 else "mla_attend_kernel",
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": hbm_traffic_record(),
+            "traffic": hbm_traffic_record(name),
             "launch_ms": attend_avg_ms,
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": tflops,
