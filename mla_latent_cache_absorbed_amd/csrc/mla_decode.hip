@@ -189,6 +189,18 @@ __device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t 
   asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(r), "{m0}"(m0));
 }
+// The same load for a staged latent row: byte offset soff (uniform) within the
+// block, and this lane's 16 bytes at lane16 ^ sw (sw uniform, the row's
+// swizzle); the per-lane offset is formed inside the asm so that no per-row
+// VGPR is live (and spilled) across the issue sequence.
+__device__ __forceinline__ void dma16_row(__amdgpu_buffer_rsrc_t r, uint32_t soff, uint32_t lane16,
+                                          uint32_t sw, const char LDS_AS* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  uint32_t tmp;
+  asm volatile("v_xor_b32 %0, %1, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %3, %4 offen lds"
+               : "=&v"(tmp)
+               : "s"(sw), "v"(lane16), "s"(r), "s"(soff), "{m0}"(m0));
+}
 __device__ __forceinline__ void dma16_global(const char* src, const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
@@ -238,8 +250,7 @@ __device__ __forceinline__ void issue_load(const AttendArgs& a, const StageIds& 
     const uint32_t blk_bytes = uint32_t(kD * 2) << lg;
     const __amdgpu_buffer_rsrc_t r =
         block_rsrc(cbase, ((tok >> lg) == id.lb0) ? id.blk0 : id.blk1, blk_bytes);
-    const uint32_t voff = uint32_t(tok & bs_mask) * (kD * 2) + (lane16 ^ uint32_t(swzA(i) * 16));
-    dma16_buffer(r, voff, sbuf + i * 1024);
+    dma16_row(r, uint32_t(tok & bs_mask) * (kD * 2), lane16, uint32_t(swzA(i) * 16), sbuf + i * 1024);
   } else {
     const int jb = w + NW * (j - kSub / NW);  // region-B load: chunks 2jb, 2jb+1
     const int t = (lane16 >> 4) & 31;
@@ -415,19 +426,27 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
       // lane holds head hl, dims 16s + 8hi .. +7 (reloaded on a redo so that
       // they are not live past the last score MFMA of a pass).
+      // Lanes of padding heads load head 0's query (their results are never
+      // written); no select follows the loads, so they all go out at once.
       bf16x8 qreg[36];
       {
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
             a.q + (size_t(b) * a.H + (head_ok ? head : 0)) * kD + 8 * hi);
 #pragma unroll
-        for (int s = 0; s < 36; ++s) {
-          bf16x8 v = qp[2 * s];
-          if (!head_ok) v = bf16x8{};
-          qreg[s] = v;
-        }
+        for (int s = 0; s < 36; ++s) qreg[s] = qp[2 * s];
       }
+      // Stage 0 goes out behind the queries, and both are waited for before
+      // the next stages go out: the compiler counts only its own (query)
+      // loads, so its waits before the score MFMAs would otherwise also wait
+      // for later stages.
+      {
+        const StageIds id = stage_ids(a, b, stage_base(0), t1, bad);
 #pragma unroll
-      for (int p = 0; p < NS - 1; ++p) {
+        for (int j = 0; j < LPW; ++j) issue_load<NW>(a, id, lds, t1, w, lane16, j);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+#pragma unroll
+      for (int p = 1; p < NS - 1; ++p) {
         const StageIds id = stage_ids(a, b, stage_base(p), t1, bad);
 #pragma unroll
         for (int j = 0; j < LPW; ++j)
@@ -435,7 +454,6 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       }
       StageIds nxt = stage_ids(a, b, stage_base(NS - 1), t1, bad);
       // stage 0 scores (a lone chain, once per item)
-      wait_vmcnt_lgkm0<LPW * (NS - 2)>();
       block_barrier();
       f32x16 sacc;
       {
@@ -1034,14 +1052,12 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
       // kernel)
       bf16x8 qreg[36];
       {
+        // padding heads load head 0's query (never written out); no select
+        // follows the loads, so they all go out at once
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
             a.q + (size_t(b) * a.H + (head_ok ? hl : 0)) * kD + 8 * hi);
 #pragma unroll
-        for (int s = 0; s < 36; ++s) {
-          bf16x8 v = qp[2 * s];
-          if (!head_ok) v = bf16x8{};
-          qreg[s] = v;
-        }
+        for (int s = 0; s < 36; ++s) qreg[s] = qp[2 * s];
       }
       for (int st = 0; st < nst; ++st) {
         const StageIds id = stage_ids(a, b, t0 + st * kSub, t1, bad);
@@ -1345,19 +1361,27 @@ __device__ __forceinline__ int plan_candidate(int i) {
 }
 
 // Inclusive block-wide scan of one int per thread; returns (inclusive, total).
+// A 64-lane shuffle scan in each wave, then the four wave totals through LDS.
 __device__ __forceinline__ int2 block_scan(int v, int* s_scan) {
-  const int tid = threadIdx.x;
-  s_scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int u = (tid >= off) ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += u;
-    __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int2 r = make_int2(s_scan[tid], s_scan[kPlanThreads - 1]);
+  if (lane == 63) s_scan[wv] = x;
   __syncthreads();
-  return r;
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanThreads / 64; ++i) {
+    const int t = s_scan[i];
+    pre += (i < wv) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  return make_int2(x + pre, tot);
 }
 
 // Items are laid out full chunks first, then the last (shorter) chunk of each
@@ -1369,7 +1393,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   __shared__ long long s_cost[kPlanThreads];
   __shared__ int s_chunk[kPlanThreads];
   __shared__ int s_scan[kPlanThreads];
-  __shared__ int s_len[kPlanLens];
+  __shared__ __attribute__((aligned(16))) int s_len[kPlanLens];
   const int tid = threadIdx.x;
   const int Lmax = M << lgBS;
 
@@ -1378,31 +1402,63 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   int chunk = forced;
   if (forced <= 0) {
     const int T = plan_candidate(tid);
+    // ceil(L / T) for T = 32 d: ceil(ceil(L / 32) / d), with the quotient from
+    // a float reciprocal (off by at most one for these sizes) and one exact
+    // correction; this keeps integer division out of the B x 256 loop.
+    const int d = T >> 5;
+    const float inv_d = 1.0f / float(d);
     long long n = 0;
     for (int b0 = 0; b0 < B; b0 += kPlanLens) {
       const int nb = min(kPlanLens, B - b0);
-      for (int i = tid; i < nb; i += kPlanThreads) s_len[i] = min(max(seq_lens[b0 + i], 0), Lmax);
+      // lengths in 32-token units, padded to a multiple of 4 with zeros
+      const int nb4 = (nb + 3) & ~3;
+      for (int i = tid; i < nb4; i += kPlanThreads)
+        s_len[i] = (i < nb) ? (min(max(seq_lens[b0 + i], 0), Lmax) + 31) >> 5 : -1;
       __syncthreads();
-      for (int i = 0; i < nb; ++i) n += max(1, (s_len[i] + T - 1) / T);
-      __syncthreads();
-    }
-    s_cost[tid] = (n <= cap) ? ((n + n_slots - 1) / n_slots) * (long long)(T + ovh) : (1ll << 62);
-    s_chunk[tid] = T;
-    __syncthreads();
-    for (int st = kPlanThreads / 2; st > 0; st >>= 1) {
-      if (tid < st) {
-        const long long c2 = s_cost[tid + st];
-        const int k2 = s_chunk[tid + st];
-        if (c2 < s_cost[tid] || (c2 == s_cost[tid] && k2 > s_chunk[tid])) {
-          s_cost[tid] = c2;
-          s_chunk[tid] = k2;
-        }
+      auto items_of = [&](int m) {
+        int q = int(float(m) * inv_d);
+        const int r = m - q * d;
+        q += (r >= d) - (r < 0);
+        const int rr = m - q * d;
+        return (m < 0) ? 0 : max(1, q + (rr > 0));  // m < 0: padding
+      };
+#pragma unroll 4
+      for (int i = 0; i < nb4; i += 4) {
+        const int4 m4 = *reinterpret_cast<const int4*>(&s_len[i]);
+        n += items_of(m4.x) + items_of(m4.y) + items_of(m4.z) + items_of(m4.w);
       }
       __syncthreads();
     }
-    chunk = s_chunk[0];
+    // cheapest candidate, the larger chunk on ties: a shuffle reduction in
+    // each wave, then over the four waves
+    long long c = (n <= cap) ? ((n + n_slots - 1) / n_slots) * (long long)(T + ovh) : (1ll << 62);
+    int k = T;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const long long c2 = __shfl_xor(c, off, 64);
+      const int k2 = __shfl_xor(k, off, 64);
+      if (c2 < c || (c2 == c && k2 > k)) {
+        c = c2;
+        k = k2;
+      }
+    }
+    if ((tid & 63) == 0) {
+      s_cost[tid >> 6] = c;
+      s_chunk[tid >> 6] = k;
+    }
+    __syncthreads();
+    long long cb = s_cost[0];
+    int kb = s_chunk[0];
+#pragma unroll
+    for (int i = 1; i < kPlanThreads / 64; ++i) {
+      if (s_cost[i] < cb || (s_cost[i] == cb && s_chunk[i] > kb)) {
+        cb = s_cost[i];
+        kb = s_chunk[i];
+      }
+    }
+    chunk = kb;
     // no candidate fits the workspace: one item per request
-    if (s_cost[0] >= (1ll << 62)) chunk = ((Lmax + 31) / 32) * 32;
+    if (cb >= (1ll << 62)) chunk = ((Lmax + 31) / 32) * 32;
     __syncthreads();
   }
 
