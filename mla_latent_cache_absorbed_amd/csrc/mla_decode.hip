@@ -819,11 +819,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     constexpr int kSlots = NS * kStageBytes / (NW * 32 * 4);
     float LDS_AS* wsl = (float LDS_AS*)(lds) + w * 32 * kSlots + (lane_m & 31);
     const bool in_lds = cnt <= kSlots;
+    // items' log-sum-exps in batches of 16, every load of a batch in flight
     float mlse = -INFINITY;
-    for (int s = 0; s < cnt; ++s) {
-      const float l = lse_of(slot_of(s));
-      mlse = fmaxf(mlse, l);
-      if (in_lds) wsl[32 * s] = l;
+    for (int s0 = 0; s0 < cnt; s0 += 16) {
+      float lv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) lv[j] = (s0 + j < cnt) ? lse_of(slot_of(s0 + j)) : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        mlse = fmaxf(mlse, lv[j]);
+        if (in_lds && s0 + j < cnt) wsl[32 * (s0 + j)] = lv[j];
+      }
     }
     float lam = 0.0f;
     for (int s = 0; s < cnt; ++s) {
@@ -1276,11 +1282,17 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     constexpr int kSlots = kStageBytes / (32 * 4);
     float LDS_AS* wsl = (float LDS_AS*)(slot) + hl_m;
     const bool in_lds = cnt <= kSlots;
+    // items' log-sum-exps in batches of 16, every load of a batch in flight
     float mlse = -INFINITY;
-    for (int s = 0; s < cnt; ++s) {
-      const float l = lse_of(slot_of(s));
-      mlse = fmaxf(mlse, l);
-      if (in_lds) wsl[32 * s] = l;
+    for (int s0 = 0; s0 < cnt; s0 += 16) {
+      float lv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) lv[j] = (s0 + j < cnt) ? lse_of(slot_of(s0 + j)) : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        mlse = fmaxf(mlse, lv[j]);
+        if (in_lds && s0 + j < cnt) wsl[32 * (s0 + j)] = lv[j];
+      }
     }
     float lam = 0.0f;
     for (int s = 0; s < cnt; ++s) {
