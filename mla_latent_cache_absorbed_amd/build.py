@@ -38,6 +38,12 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    # MFMAs issued from inline asm: the compiler cannot see their operand
+    # hazards, so the compiled code is checked for them
+    from mla_latent_cache_absorbed_amd import isa_check
+    probs = isa_check.check_source(SRC, HIPCC, [*FLAGS, *extra])
+    if probs:
+        raise RuntimeError("MFMA operand hazards in the compiled code:\n" + "\n".join(probs))
     return LIB
 
 

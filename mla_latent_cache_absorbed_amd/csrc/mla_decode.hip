@@ -48,8 +48,12 @@ constexpr int kMaxExtraItems = 1024;      // work items beyond B the workspace h
 constexpr int kHdrBytes = 256;
 constexpr float kRefHeadroom = 64.0f;     // log2 units: P <= 2^64 before an item is redone
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr int kSc1 = 16;                  // cache-policy bit: agent-coherent access
+constexpr int kSc1 = 16;                  // cache-policy bit sc1: agent-scope coherent access
 constexpr int kMergeMinItems = 3;         // splits this wide are merged by merge units
+// Per-request counters: tickets taken (or merge units done) and partials
+// published.  Both are 0 between calls.
+constexpr int kCtr = 2;
+enum { kTicket = 0, kPublished = 1 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -77,7 +81,7 @@ __host__ __device__ inline WsLayout ws_layout(int B, int H) {
   w.cap = B + kMaxExtraItems;
   w.req_off = kHdrBytes;
   w.ctr_off = align256(w.req_off + size_t(B) * 16);
-  w.big_off = align256(w.ctr_off + size_t(B) * 8);
+  w.big_off = align256(w.ctr_off + size_t(B) * kCtr * 4);
   w.item_off = align256(w.big_off + size_t(B) * 4);
   w.plse_off = align256(w.item_off + size_t(w.cap) * 16);
   w.po_off = align256(w.plse_off + size_t(w.cap) * hp * 4);
@@ -120,25 +124,85 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// No divergent regions while accumulators are live.  The compiler has been
+// seen to place copies of live registers inside a region entered with part
+// of the wave masked off, which copies only the active lanes.  So the attend
+// kernels never branch on a lane index: a single-lane atomic sets and
+// restores the exec mask inside one asm statement (callers run with the whole
+// wave active), polls are made by every lane with a uniform exit, and a store
+// that only some lanes need is made by all lanes with identical values or
+// falls outside its buffer resource.
+
+// Lane 0 adds v to *p (relaxed, agent scope); returns the old value.
+__device__ __forceinline__ int lane0_fetch_add(int32_t* p, int v) {
+  int old, res;
+  uint64_t keep;
+  asm volatile(
+      "s_mov_b64 %2, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %0, %3, %4, off sc0\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_mov_b64 exec, %2\n\t"
+      "v_readlane_b32 %1, %0, 0\n\t"
+      "s_nop 4"
+      : "=&v"(old), "=s"(res), "=&s"(keep)
+      : "v"(p), "v"(v)
+      : "memory");
+  return res;
+}
+// Lane 0 ors v into *p (relaxed, agent scope).
+__device__ __forceinline__ void lane0_atomic_or(int32_t* p, int v) {
+  uint64_t keep;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_or %1, %2, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(keep)
+      : "v"(p), "v"(v)
+      : "memory");
+}
+// Every lane of the wave polls *p until it reaches target; the exit is
+// uniform.  Bounded: past the bound `flag` is raised in *flags.
+__device__ __forceinline__ void wave_poll(int32_t* p, int target, int32_t* flags, int flag) {
+  for (int spin = 0;; ++spin) {
+    const int v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= target) break;
+    if (spin >= (1 << 22)) {
+      lane0_atomic_or(flags, flag);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // MFMAs of the hot loop are written out so that register classes are pinned:
-// the 16 output accumulators of a wave (32 heads x 512 columns, fp32) fill
-// all 256 AGPRs and the score accumulator lives in VGPRs.  Left to itself
-// the compiler gives every MFMA builtin of a kernel this size the AGPR form
-// and then spills.  Hazards the compiler cannot see through inline asm are
-// covered here: every MFMA is preceded by two wait states (a VALU write of an
-// operand just before it); back-to-back accumulation into the same
-// registers needs none; the drains provide >= 19 wait states between the
-// last XDL write of an accumulator and any non-MFMA access to it.
+// the 16 output accumulators of a wave (512 values per lane, fp32) fill all
+// 256 AGPRs and the score accumulator lives in VGPRs.  Left to itself the
+// compiler gives every MFMA builtin of a kernel this size the AGPR form and
+// then spills.  The compiler cannot see the hazards of asm it does not parse:
+//   * an MFMA reading a register that a VALU instruction wrote needs two wait
+//     states.  Operands that come from LDS or global loads never do, so the
+//     plain forms carry no nop; pv_mfma_v, for weights just converted by the
+//     VALU, does.  isa_check.py scans the compiled code for any VALU write of
+//     an MFMA operand closer than that and fails the build;
+//   * back-to-back accumulation into the same registers needs none;
+//   * the drains provide >= 19 wait states between the last XDL write of an
+//     accumulator and any non-MFMA access to it.
 __device__ __forceinline__ void qk_mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
 __device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void pv_mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void pv_drain(f32x16 (&o)[16]) {
@@ -156,7 +220,7 @@ struct AttendArgs {
   float* lse;
   int32_t* hdr;          // workspace header (n_items, chunk, check bits, queue)
   const int4* req;       // per request: first full item, full count, remainder item, count
-  int32_t* ctr;          // per request: [tickets taken, partials published] (0 between calls)
+  int32_t* ctr;          // per request: kCtr counters (0 between calls)
   const int32_t* big;    // requests whose split is merged by merge units
   const int4* items;     // per item: request, first token, end token, request's item count
   float* part_lse;       // [cap, Hp]  log2-domain log-sum-exp of each split item
@@ -186,7 +250,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* cache, 
 __device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                              const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  // sc1: agent-scope coherent, for partials another compute unit published
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen sc1 lds"
                :: "v"(voff), "s"(r), "{m0}"(m0));
 }
 // The same load for a staged latent row: byte offset soff (uniform) within the
@@ -262,27 +327,94 @@ __device__ __forceinline__ void issue_load(const AttendArgs& a, const StageIds& 
   }
 }
 
+// With blocks of 32 tokens or more a stage (32 tokens from a multiple of 32)
+// lies inside one physical block, so one buffer resource and two row offsets
+// serve every load of it and each load takes a few instructions.
+struct StageOne {
+  __amdgpu_buffer_rsrc_t r;  // the stage's physical block
+  uint32_t row0;             // byte offset of the stage's first row in the block
+  uint32_t rowlast;          // byte offset of its last row before t1: later rows load that one
+};
+__device__ __forceinline__ StageOne stage_one(const AttendArgs& a, int b, int base, int t1, int& bad) {
+  const CONST_AS int32_t* trow = (const CONST_AS int32_t*)(a.table) + size_t(b) * a.M;
+  int blk = trow[base >> a.lgBS];
+  if ((unsigned)blk >= (unsigned)a.NB) { blk = 0; bad = 1; }
+  StageOne s;
+  s.r = block_rsrc(reinterpret_cast<const char*>(a.cache), blk, uint32_t(kD * 2) << a.lgBS);
+  s.row0 = uint32_t(base & ((1 << a.lgBS) - 1)) * (kD * 2);
+  s.rowlast = s.row0 + uint32_t(min(t1 - 1 - base, kSub - 1)) * (kD * 2);
+  return s;
+}
+// Row load with the swizzle given as a constant: lane_sw is this lane's 16
+// bytes xor the swizzle of the wave's first row (swzA is linear over bit
+// xor, and row w + NW j = w ^ NW j), sw the swizzle of NW j.
+__device__ __forceinline__ void dma16_row_c(__amdgpu_buffer_rsrc_t r, uint32_t soff, uint32_t lane_sw,
+                                            int sw, const char LDS_AS* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  uint32_t tmp;
+  asm volatile("v_xor_b32 %0, %1, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %3, %4 offen lds"
+               : "=&v"(tmp)
+               : "i"(sw), "v"(lane_sw), "s"(r), "s"(soff), "{m0}"(m0));
+}
+__device__ __forceinline__ void dma16_plain(__amdgpu_buffer_rsrc_t r, uint32_t voff, const char LDS_AS* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voff), "s"(r), "{m0}"(m0));
+}
+// Load j of this wave's share of a one-block stage (as issue_load).
+// rb_tok: this lane's region-B token times the row size; rb_cp: 1024 plus
+// its 16-byte chunk within a pair.
+template <int NW>
+__device__ __forceinline__ void issue_one(const StageOne& s, char LDS_AS* sbuf, int w, uint32_t lane_sw,
+                                          uint32_t rb_tok, uint32_t rb_cp, int j) {
+  if (j < kSub / NW) {
+    const int i = w + NW * j;
+    dma16_row_c(s.r, min(s.row0 + uint32_t(i) * (kD * 2), s.rowlast), lane_sw, swzA(NW * j) * 16,
+                sbuf + i * 1024);
+  } else {
+    const int jb = w + NW * (j - kSub / NW);  // k_rope chunks 2jb, 2jb+1 of all 32 tokens
+    dma16_plain(s.r, min(s.row0 + rb_tok, s.rowlast) + rb_cp + 32 * jb, sbuf + kRegionB + jb * 1024);
+  }
+}
+
 template <bool V>
 struct BoolC {
   static constexpr bool value = V;
 };
+template <bool C, class A, class B>
+struct Pick {
+  using T = A;
+};
+template <class A, class B>
+struct Pick<false, A, B> {
+  using T = B;
+};
 
-constexpr int kMergeSpinLimit = 1 << 22;  // polls for the partners of a split merge
 constexpr int kWaveBytesM = 32 * kDV * 4;  // one wave's share of an item's partial
 
-template <int NW, int NS>
+// kOne: the block size is 32 tokens or more, so every stage lies in one block.
+template <int NW, int NS, bool kOne>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
-  static_assert(NW == 1 || NW == 2 || NW == 4, "waves per workgroup");
+  static_assert(NW == 2 || NW == 4, "waves per workgroup");
   static_assert(NS >= 3, "the pipeline reads two stages while one more loads");
-  __shared__ __attribute__((aligned(1024))) char lds_raw[NS * kStageBytes];
-  __shared__ int s_item;
-  __shared__ int s_ticket;
-  char LDS_AS* lds = (char LDS_AS*)(lds_raw);
-
   constexpr int LPW = kLoadsPerStage / NW;  // loads per wave per stage
   constexpr int PFK = 4;                    // score operand reads in flight
   constexpr int PFV = 2;                    // weighted-sum operand reads in flight
   constexpr int HP = NW * 32;               // heads covered by the workgroup
+  constexpr int CPW = 16 / NW;              // 32-column blocks of O per wave
+  constexpr int PBUF = NW * 2 * 1024;       // one stage's weights P (bf16)
+  // LDS: the stage ring, then two buffers of weights.  Outside the stage loop
+  // the first weight buffer holds instead the per-head row sums and
+  // log-sum-exps being exchanged, the waves' redo votes and two scalars.
+  __shared__ __attribute__((aligned(1024))) char lds_raw[NS * kStageBytes + 2 * PBUF];
+  char LDS_AS* lds = (char LDS_AS*)(lds_raw);
+  char LDS_AS* const pw = lds + NS * kStageBytes;
+  float LDS_AS* const x_l = (float LDS_AS*)pw;          // [HP] row sums
+  float LDS_AS* const x_lse = x_l + HP;                 // [HP] log2-domain log-sum-exps
+  int LDS_AS* const s_vote = (int LDS_AS*)(x_lse + HP);  // [NW] redo votes
+  int LDS_AS* const s_item = s_vote + NW;               // fetched item or merge unit
+  int LDS_AS* const s_ticket = s_item + 1;              // ticket of a two-item split
+  static_assert((2 * HP + NW + 2) * 4 <= PBUF, "exchange area");
+
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int hl = lane & 31;
@@ -310,9 +442,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     for (int j = 0; j < 8; ++j) qk_off[j] = hl * 1024 + ((((2 * j) | hi)) ^ xa) * 16;
   }
   const int qkb = kRegionB + hi * 512 + hl * 16;
-  // PV transposed reads: lane reads token 16kk + 8e + 4hi + r, chunk 4cb + cc,
-  // half u0 (r = lane bits 3:2, cc = 2*bit4 + bit1, u0 = bit0) at
-  // pv_off[e][cb & 3] + 16384 kk + 256 (cb >> 2).
+  // Weighted sum.  Wave w owns columns 32 CPW w .. 32 CPW (w + 1) - 1 of O
+  // for all HP heads: accumulator o[hb CPW + c] is O^T of the 32 columns of
+  // block cb = CPW w + c for heads 32 hb .. 32 hb + 31.  So each wave reads
+  // only its slab of V, and the weights P of all heads go through LDS.
+  // V fragment f (kk = f / CPW, c = f % CPW) is V^T of block cb over the 16
+  // tokens of half kk, read transposed: the lane reads token 16 kk + 8 e +
+  // 4 hi + r, chunk 4 cb + cc, half u0 (r = lane bits 3:2, cc = 2 bit4 +
+  // bit1, u0 = bit0) at pv_off[e][c & 3] + 16384 kk + 256 (c >> 2).
   int pv_off[2][4];
   {
     const int r = (lane >> 2) & 3;
@@ -323,9 +460,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       const int T = 8 * e + 4 * hi + r;
       const int sa = swzA(T);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pv_off[e][j] = T * 1024 + (((4 * j) | cc) ^ sa) * 16 + 8 * u0;
+      for (int j = 0; j < 4; ++j)
+        pv_off[e][j] = T * 1024 + (((4 * j) | cc) ^ sa) * 16 + 8 * u0 + 256 * (CPW / 4) * w;
     }
   }
+  // P fragment (hb, kk): the B operand of the weighted sum for heads of
+  // block hb over token half kk, as wave hb's lanes hold it (head 32 hb +
+  // lane % 32, the same 8 tokens per lane as the V fragments); 1 KB
+  // contiguous at (2 hb + kk) KB of a weight buffer.
+  const int p_lane = lane * 16;
 
   // Workgroup g takes item g directly; items grid, grid+1, ... come from the
   // queue.  With no more items than workgroups no atomic is needed at all.
@@ -338,12 +481,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     int it = int(blockIdx.x);
     if (!first) {
       if (n_items <= grid) break;
-      if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[3], 1);
+      if (w == 0) {
+        const int f = lane0_fetch_add(&a.hdr[3], 1);
+        *s_item = f;
+      }
       __syncthreads();
-      const int v = __builtin_amdgcn_readfirstlane(s_item);
+      const int v = __builtin_amdgcn_readfirstlane(*s_item);
       __syncthreads();
       if (v + grid >= n_items) {
-        if (threadIdx.x == 0 && v == n_items - 1) atomicExch(&a.hdr[3], 0);
+        if (w == 0 && v == n_items - 1) __hip_atomic_store(&a.hdr[3], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       it = v + grid;
@@ -362,18 +508,18 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       int lane_z = lane;
       asm volatile("" : "+v"(lane_z));
       const int head_z = w * 32 + (lane_z & 31);
-      if (head_z < a.H) {
-        const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(a.out + (size_t(b) * a.H + w * 32) * kDV), (short)0,
-            (a.H - w * 32) * kDV * 2, 0x00020000);
-        const uint32_t zoff = uint32_t((lane_z & 31) * kDV + 4 * (lane_z >> 5)) * 2;
+      // lanes of heads >= H fall outside both resources
+      const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t zl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
+      const uint32_t zoff = uint32_t(head_z * kDV + 4 * (lane_z >> 5)) * 2;
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, zr, zoff + (32 * cb + 8 * g) * 2, 0, 0);
-        if ((lane_z >> 5) == 0) a.lse[size_t(b) * a.H + head_z] = -INFINITY;
-      }
+        for (int g = 0; g < 4; ++g)
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, zr, zoff + (32 * cb + 8 * g) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), zl, uint32_t(head_z) * 4, 0, 0);
       continue;
     }
     const int nst = (t1 - t0 + kSub - 1) / kSub;
@@ -385,20 +531,23 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     float m_run = -INFINITY;  // exponent reference of this head (log2 units)
     float amax = -INFINITY;   // largest exponent argument (score * c2 - m_run) of this lane
     float la = 0.0f, lb = 0.0f;  // this lane's share of the row sum, in two chains
+    bool first_pass = true;   // uniform: false on a redo
 
 #define MLA_KREAD(sb, s)                                                               \
   ((s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))      \
             : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
-#define MLA_VREAD(sb, n, dst)                                                               \
+#define MLA_VREAD(sb, f, dst)                                                               \
   do {                                                                                      \
-    const int cb_ = (n) & 15, kk_ = (n) >> 4;                                               \
-    const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                        \
+    const int c_ = (f) % CPW, kk_ = (f) / CPW;                                              \
+    const int imm_ = kk_ * 16384 + 256 * (c_ >> 2);                                         \
     const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)((sb) + pv_off[0][cb_ & 3] + imm_));                                \
+        (bf16x4 LDS_AS*)((sb) + pv_off[0][c_ & 3] + imm_));                                 \
     const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)((sb) + pv_off[1][cb_ & 3] + imm_));                                \
+        (bf16x4 LDS_AS*)((sb) + pv_off[1][c_ & 3] + imm_));                                 \
     dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
   } while (0)
+#define MLA_PREAD(pb, hb, kk) (*(const bf16x8 LDS_AS*)((pb) + ((hb) * 2 + (kk)) * 1024 + p_lane))
+#define MLA_PWRITE(pb, kk, val) (*(bf16x8 LDS_AS*)((pb) + (w * 2 + (kk)) * 1024 + p_lane) = (val))
 
     // ---- stage pipeline ----
     // Each head's exponent reference m_run is fixed from the item's first
@@ -410,18 +559,35 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // reference.  With the reference fixed, a stage's weights need no
     // cross-lane step, so its softmax runs in the shadow of MFMAs.
     //
-    // Iteration k holds P(k).  Phase 1 runs the 36 score MFMAs of stage k+1
-    // interleaved with the first 16 weighted-sum MFMAs of stage k, and issues
-    // this wave's loads of stage k+NS-1 spread between them; phase 2 runs the
-    // other 16 weighted-sum MFMAs with the softmax of stage k+1 between them.
-    // Stages k+2 .. k+NS-2 stay in flight.  Every iteration issues a full
-    // stage (past the item's end, a copy of its last stage into a free slot)
-    // so that one wait count serves all iterations.  Only a request's last
-    // stage can be partial, so only the last iteration applies the mask.
+    // Iteration k finds P(k) of all heads in weight buffer k % 2.  Phase 1
+    // runs the 36 score MFMAs of stage k+1 interleaved with the 16
+    // weighted-sum MFMAs of stage k's first token half, and issues this
+    // wave's loads of stage k+NS-1 spread between them; phase 2 runs the 16
+    // of the second half with the softmax of stage k+1 between them, whose
+    // weights go to the other buffer.  Stages k+2 .. k+NS-2 stay in flight.
+    // Every iteration issues a full stage (past the item's end, a copy of its
+    // last stage into a free slot) so that one wait count serves all
+    // iterations.  Only a request's last stage can be partial, so only the
+    // last iteration applies the mask.
+    //
+    // Weighted-sum MFMA n (0..31) of a stage uses V fragment f = n / NW with
+    // the P fragment of head block hb = n % NW, into o[hb CPW + f % CPW].
     uint32_t lane16 = uint32_t(lane) * 16;
+    uint32_t lane_sw = lane16 ^ uint32_t(swzA(w) * 16);
+    uint32_t rb_tok = ((lane16 >> 4) & 31) * (kD * 2);
+    uint32_t rb_cp = 1024 + (lane16 >> 9) * 16;
     // keep the per-lane load offsets from being hoisted out of the item loop
-    asm volatile("" : "+v"(lane16));
+    asm volatile("" : "+v"(lane16), "+v"(lane_sw), "+v"(rb_tok), "+v"(rb_cp));
     auto stage_base = [&](int p) { return t0 + min(p, nst - 1) * kSub; };
+    using Src = typename Pick<kOne, StageOne, StageIds>::T;
+    auto src_of = [&](int base) -> Src {
+      if constexpr (kOne) return stage_one(a, b, base, t1, bad);
+      else return stage_ids(a, b, base, t1, bad);
+    };
+    auto issue = [&](const Src& sr, char LDS_AS* sbuf, int j) {
+      if constexpr (kOne) issue_one<NW>(sr, sbuf, w, lane_sw, rb_tok, rb_cp, j);
+      else issue_load<NW>(a, sr, sbuf, t1, w, lane16, j);
+    };
     for (;;) {
       // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
       // lane holds head hl, dims 16s + 8hi .. +7 (reloaded on a redo so that
@@ -440,19 +606,18 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       // loads, so its waits before the score MFMAs would otherwise also wait
       // for later stages.
       {
-        const StageIds id = stage_ids(a, b, stage_base(0), t1, bad);
+        const Src id = src_of(stage_base(0));
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) issue_load<NW>(a, id, lds, t1, w, lane16, j);
+        for (int j = 0; j < LPW; ++j) issue(id, lds, j);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
 #pragma unroll
       for (int p = 1; p < NS - 1; ++p) {
-        const StageIds id = stage_ids(a, b, stage_base(p), t1, bad);
+        const Src id = src_of(stage_base(p));
 #pragma unroll
-        for (int j = 0; j < LPW; ++j)
-          issue_load<NW>(a, id, lds + p * kStageBytes, t1, w, lane16, j);
+        for (int j = 0; j < LPW; ++j) issue(id, lds + p * kStageBytes, j);
       }
-      StageIds nxt = stage_ids(a, b, stage_base(NS - 1), t1, bad);
+      Src nxt = src_of(stage_base(NS - 1));
       // stage 0 scores (a lone chain, once per item)
       block_barrier();
       f32x16 sacc;
@@ -471,18 +636,18 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       }
       // register v holds token 4hi + 8(v/4) + (v%4) of its stage: valid
       // while 8(v/4) + (v%4) < (stage end) - 4hi
-      bf16x8 p0, p1;
-      bf16x8 vf[PFV];  // weighted-sum operands, read one phase ahead
+      bf16x8 vf[PFV];  // weighted-sum operands, read ahead
       {
         const int lim = t1 - t0 - 4 * hi;
-        if (m_run == -INFINITY) {
-          // first pass: the reference is the head's largest stage-0 score
+        if (first_pass) {
+          // the reference is the head's largest stage-0 score
           float mx = -INFINITY;
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            if (8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, sacc[v] * c2);
+            mx = fmaxf(mx, (8 * (v >> 2) + (v & 3) < lim) ? sacc[v] * c2 : -INFINITY);
           m_run = pair_max(mx);
         }
+        bf16x8 p0, p1;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const float arg = (8 * (v >> 2) + (v & 3) < lim) ? fmaf(sacc[v], c2, -m_run) : -INFINITY;
@@ -493,6 +658,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           if (v < 8) p0[v] = (__bf16)pv;
           else p1[v - 8] = (__bf16)pv;
         }
+        MLA_PWRITE(pw, 0, p0);
+        MLA_PWRITE(pw, 1, p1);
 #pragma unroll
         for (int s = 0; s < PFV; ++s) MLA_VREAD(lds, s, vf[s]);
       }
@@ -501,42 +668,43 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         constexpr bool kMask = decltype(mask_tag)::value;
         constexpr int kDmaEvery = 36 / LPW;  // score MFMAs per load issued
         const char LDS_AS* sbv = lds + (k % NS) * kStageBytes;
-        // stage k+1 must be in LDS; stage k+2 may still be loading
+        const char LDS_AS* pcur = pw + (k & 1) * PBUF;
+        char LDS_AS* pnxt = pw + ((k + 1) & 1) * PBUF;
+        // stage k+1 and every wave's P(k) must be in LDS; stage k+2 may
+        // still be loading
         wait_vmcnt_lgkm0<LPW * (NS - 3)>();
         block_barrier();
-        const StageIds cur = nxt;
+        const Src cur = nxt;
         char LDS_AS* sdst = lds + ((k + NS - 1) % NS) * kStageBytes;
-        nxt = stage_ids(a, b, stage_base(k + NS), t1, bad);
+        nxt = src_of(stage_base(k + NS));
         const char LDS_AS* sbk = lds + ((k + 1) % NS) * kStageBytes;
         // With four waves each issues 9 loads per stage, spread between the
-        // score MFMAs; a lone or paired wave issues its 36 or 18 in a burst
-        // (spread that thin, every stall of the memory pipeline would land
-        // on an MFMA).
+        // score MFMAs; a pair of waves issues its 18 in a burst (spread that
+        // thin, every stall of the memory pipeline would land on an MFMA).
         constexpr bool kSpread = NW == 4;
         if (!kSpread)
 #pragma unroll
-          for (int j = 0; j < LPW; ++j) issue_load<NW>(a, cur, sdst, t1, w, lane16, j);
+          for (int j = 0; j < LPW; ++j) issue(cur, sdst, j);
         bf16x8 kf[PFK];
 #pragma unroll
         for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sbk, s);
-        // phase 1: two weighted-sum MFMAs (operands already in registers)
-        // cover the first score reads; then score, score, weighted-sum ...
+        bf16x8 pa[NW], pb[NW];  // P(k) fragments of the two token halves
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          pv_mfma(o[n], vf[n % PFV], p0);
-          MLA_VREAD(sbv, n + PFV, vf[n % PFV]);
-        }
+        for (int h = 0; h < NW; ++h) pa[h] = MLA_PREAD(pcur, h, 0);
+        auto pv_step = [&](int n) {
+          const int f = n / NW, h = n % NW;
+          pv_mfma(o[h * CPW + f % CPW], vf[f % PFV], n < 16 ? pa[h] : pb[h]);
+          if (h == NW - 1 && f + PFV < 2 * CPW) MLA_VREAD(sbv, f + PFV, vf[f % PFV]);
+          if (n >= 16 - NW && n < 16) pb[h] = MLA_PREAD(pcur, h, 1);
+        };
+        // phase 1
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
           if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
           else qk_mfma(sacc, kf[s % PFK], qreg[s]);
           if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sbk, s + PFK);
-          if (kSpread && s % kDmaEvery == 0) issue_load<NW>(a, cur, sdst, t1, w, lane16, s / kDmaEvery);
-          if ((s & 1) && (s >> 1) + 2 < 16) {
-            const int n = (s >> 1) + 2;
-            pv_mfma(o[n], vf[n % PFV], p0);
-            MLA_VREAD(sbv, n + PFV, vf[n % PFV]);
-          }
+          if (kSpread && s % kDmaEvery == 0) issue(cur, sdst, s / kDmaEvery);
+          if ((s & 1) && (s >> 1) < 16) pv_step(s >> 1);
         }
         qk_drain(sacc);
         // phase 2
@@ -544,9 +712,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         bf16x8 n0, n1;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int n = 16 + v;
-          pv_mfma(o[v], vf[n % PFV], p1);
-          if (n + PFV < 32) MLA_VREAD(sbv, n + PFV, vf[n % PFV]);
+          pv_step(16 + v);
           float arg = fmaf(sacc[v], c2, -m_run);
           if (kMask) arg = (8 * (v >> 2) + (v & 3) < lim) ? arg : -INFINITY;
           amax = fmaxf(amax, arg);
@@ -555,10 +721,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           else la += pv;
           if (v < 8) n0[v] = (__bf16)pv;
           else n1[v - 8] = (__bf16)pv;
+          if (v == 7) MLA_PWRITE(pnxt, 0, n0);
+          if (v == 15) MLA_PWRITE(pnxt, 1, n1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        p0 = n0;
-        p1 = n1;
         // operands of the next weighted sum (stage k+1, already in LDS)
 #pragma unroll
         for (int s = 0; s < PFV; ++s) MLA_VREAD(sbk, s, vf[s]);
@@ -566,22 +732,39 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       for (int k = 0; k + 2 < nst; ++k) iteration(k, BoolC<false>{});
       if (nst >= 2) iteration(nst - 2, BoolC<true>{});
       {
-        // weighted sum of the last stage
+        // weighted sum of the last stage, once every wave's weights are in
         const char LDS_AS* sbv = lds + ((nst - 1) % NS) * kStageBytes;
+        const char LDS_AS* pcur = pw + ((nst - 1) & 1) * PBUF;
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        block_barrier();
+        bf16x8 pa[NW], pb[NW];
 #pragma unroll
-        for (int s = 0; s < 32; ++s) {
-          pv_mfma(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
-          if (s + PFV < 32) MLA_VREAD(sbv, s + PFV, vf[s % PFV]);
+        for (int h = 0; h < NW; ++h) pa[h] = MLA_PREAD(pcur, h, 0);
+#pragma unroll
+        for (int n = 0; n < 32; ++n) {
+          const int f = n / NW, h = n % NW;
+          pv_mfma(o[h * CPW + f % CPW], vf[f % PFV], n < 16 ? pa[h] : pb[h]);
+          if (h == NW - 1 && f + PFV < 2 * CPW) MLA_VREAD(sbv, f + PFV, vf[f % PFV]);
+          if (n >= 16 - NW && n < 16) pb[h] = MLA_PREAD(pcur, h, 1);
         }
       }
       // Copies issued past the item's end are drained and all waves are done
-      // reading the ring before it is refilled.
+      // reading the ring and the weights before either is reused.
       wait_vmcnt_lgkm0<0>();
       block_barrier();
-      if (!__syncthreads_or(amax > kRefHeadroom)) break;
+      {
+        const bool vote = __ballot(amax > kRefHeadroom) != 0;
+        s_vote[w] = vote ? 1 : 0;
+      }
+      __syncthreads();
+      int redo = 0;
+#pragma unroll
+      for (int h = 0; h < NW; ++h) redo |= s_vote[h];
+      if (!__builtin_amdgcn_readfirstlane(redo)) break;
       // Redo the item from its first stage with the head's largest score as
       // the reference.
       m_run += pair_max(amax);
+      first_pass = false;
       amax = -INFINITY;
       la = 0.0f;
       lb = 0.0f;
@@ -591,8 +774,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     }
 #undef MLA_KREAD
 #undef MLA_VREAD
+#undef MLA_PREAD
+#undef MLA_PWRITE
     pv_drain(o);
-    if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
+    if (__builtin_amdgcn_readfirstlane(bad)) lane0_atomic_or(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
 
     // ---- finalize ----
     // Per-lane offsets of the epilogue derive from an opaque copy of the
@@ -605,68 +790,82 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     const int head_e = w * 32 + hl_e;
     const float l_tot = pair_sum(la + lb);
     const float lse2 = m_run + log2f(l_tot);  // log2 of sum_t 2^(scaled score)
-    const float own_inv = 1.0f / l_tot;
-    // out and lse of request b through buffer resources (32-bit lane offsets)
+    // every wave needs the row sums (and a merger the log-sum-exps) of all
+    // heads of its slab; lanes l and l + 32 hold the same values
+    x_l[head_e] = l_tot;
+    x_lse[head_e] = lse2;
+    __syncthreads();
+    float inv[NW];
+#pragma unroll
+    for (int h = 0; h < NW; ++h) inv[h] = 1.0f / x_l[h * 32 + hl_e];
+    // out and lse of request b through buffer resources (32-bit lane
+    // offsets); stores past the request's H heads fall outside the resource
+    // and are dropped
     const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
-    const uint32_t out_off = uint32_t(head_e * kDV + 4 * hi_e) * 2;
-    // bf16 of 4 consecutive columns 32cb + 8g + 4hi .. +3 of this lane's head
-    auto store_out4 = [&](int cb, int g, const float (&v)[4]) {
+    const uint32_t out_off = uint32_t(hl_e * kDV + 4 * hi_e + 32 * CPW * w) * 2;
+    // bf16 of columns 32 (CPW w + c) + 8 g + 4 hi .. +3 of head 32 h + hl
+    auto store_out4 = [&](int h, int c, int g, const float (&v)[4]) {
       bf16x4 h4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) h4[r] = (__bf16)v[r];
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
-                                            out_off + (32 * cb + 8 * g) * 2, 0, 0);
+                                            out_off + (h * 32 * kDV + 32 * c + 8 * g) * 2, 0, 0);
     };
     if (cnt == 1) {
-      if (head_ok) {
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int h = 0; h < NW; ++h)
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * g + r] * own_inv;
-            store_out4(cb, g, v);
+            for (int r = 0; r < 4; ++r) v[r] = o[h * CPW + c][4 * g + r] * inv[h];
+            store_out4(h, c, g, v);
           }
-        if (hi_e == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2), lse_r, head_e * 4, 0, 0);
-      }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2), lse_r, head_e * 4, 0, 0);
       continue;
     }
 
-    // Split request.  Partials are stored in the waves' accumulator layout
-    // (each store instruction writes 1 KB contiguous; a merging wave reads
-    // back the same lanes' values), with agent-coherent (sc1) accesses, so
-    // items on different XCDs exchange them without writing back or
-    // invalidating whole L2 caches.  A request split in two is merged by its
-    // last item; wider splits by merge units once the item queue is empty.
-    constexpr int kWaveBytes = 32 * kDV * 4;  // one wave's share of a partial
+    // Split request.  An item's partial is HP x 512 fp32 in 1 KB blocks:
+    // block (h, cb, g) at byte (64 h + 4 cb + g) KB holds, in lane l's 16
+    // bytes, columns 32 cb + 8 g + 4 (l / 32) .. +3 of head 32 h + l % 32:
+    // the accumulator layout, so that each store instruction writes 1 KB
+    // contiguous and a merging wave reads back the same lanes' values.
+    // Partials are written and read with sc1 accesses, which are coherent at
+    // agent scope (the form that relaxed agent-scope atomics take), so items
+    // on different XCDs exchange them without writing back or invalidating
+    // whole L2 caches; an item counts itself published only after its
+    // stores have completed.  A request split in two is merged by its last
+    // item; wider splits by merge units once the item queue is empty.
     auto part_rsrc = [&](int slot) {
       return __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.part_o + (size_t(slot) * HP + w * 32) * kDV), (short)0, kWaveBytes, 0x00020000);
+          (void*)(a.part_o + size_t(slot) * HP * kDV), (short)0, HP * kDV * 4, 0x00020000);
     };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
-    const uint32_t lane_off = uint32_t(lane_e) * 16;
+    // this lane's 16 bytes of block (h, CPW w + c, g): slab + (64 h + 4 c + g) KB
+    const uint32_t slab = uint32_t(4 * CPW * w) * 1024 + uint32_t(lane_e) * 16;
     auto publish = [&]() {
       const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb)
+      for (int h = 0; h < NW; ++h)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v4;
+        for (int c = 0; c < CPW; ++c)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
-          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
-        }
-      if (hi_e == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v4[r] = o[h * CPW + c][4 * g + r] * inv[h];
+            __builtin_amdgcn_raw_buffer_store_b128(v4, pr, slab + (64 * h + 4 * c + g) * 1024, 0, kSc1);
+          }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's partial is out
       __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(&a.ctr[2 * b + 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (w == 0) lane0_fetch_add(&a.ctr[kCtr * b + kPublished], 1);
     };
     if (cnt >= kMergeMinItems) {
       publish();
@@ -675,10 +874,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // Two items: the item takes its ticket first; the first publishes and
     // waits no further, the last waits until its partner has published and
     // merges.
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&a.ctr[2 * b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w == 0) {
+      const int t = lane0_fetch_add(&a.ctr[kCtr * b + kTicket], 1);
+      *s_ticket = t;
+    }
     __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+    const int ticket = __builtin_amdgcn_readfirstlane(*s_ticket);
     if (ticket == 0) {
       publish();
       continue;
@@ -686,18 +887,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // The partner took its ticket earlier, so it is past its stage loop and
     // only has stores left; the wait ends.  It is bounded all the same, and
     // a flag is raised if the bound is hit.
-    if (threadIdx.x == 0) {
-      for (int spin = 0;; ++spin) {
-        if (__hip_atomic_load(&a.ctr[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= 1) break;
-        if (spin >= kMergeSpinLimit) {
-          atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      // leave both counters ready for the next call
-      __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w == 0) {
+      wave_poll(&a.ctr[kCtr * b + kPublished], 1, &a.hdr[2], MLA_CHECK_MERGE_WAIT);
+      // leave the counters ready for the next call
+      __hip_atomic_store(&a.ctr[kCtr * b + kTicket], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctr[kCtr * b + kPublished], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     {
@@ -708,60 +902,79 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       // which item finished last.
       const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
       auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
-      auto lse_of = [&](int slot) {
-        return slot == it ? lse2
-                          : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                plse_r, uint32_t(slot * HP + head_e) * 4, 0, kSc1));
-      };
       const int s0 = slot_of(0), s1 = slot_of(1);
-      const float l0 = lse_of(s0), l1 = lse_of(s1);
-      const float mlse = fmaxf(l0, l1);
-      const float e0 = __builtin_amdgcn_exp2f(l0 - mlse), e1 = __builtin_amdgcn_exp2f(l1 - mlse);
-      const float lam = e0 + e1;
-      const float inv = 1.0f / lam;
-      const float w0 = e0 * inv, w1 = e1 * inv;
       const bool own_first = s0 == it;
-      const __amdgpu_buffer_rsrc_t pr = part_rsrc(own_first ? s1 : s0);
-      // The partner's partial (64 blocks of 1 KB per wave) comes in through
-      // this wave's 36 KB of the LDS ring, free now, with direct-to-LDS loads
-      // in two rounds: every load of a round is in flight at once, and the
-      // blocks land in LDS in the layout they were stored in.
+      const int other = own_first ? s1 : s0;
+      const __amdgpu_buffer_rsrc_t pr = part_rsrc(other);
+      // The partner's blocks of this wave's slab come in through this wave's
+      // 36 KB of the LDS ring, free now, with direct-to-LDS loads in rounds
+      // of up to 36: every load of a round is in flight at once, and the
+      // blocks land in LDS in the layout they were stored in.  The
+      // log-sum-exps load meanwhile.
       char LDS_AS* mb = lds + w * kStageBytes;
       constexpr int kRound = kStageBytes / 1024;  // 36 blocks
+      constexpr int kBlocks = NW * CPW * 4;       // 64 blocks per wave
+      auto blk_off = [&](int j) {  // block j = (h, c, g) of this wave's slab
+        const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+        return slab + uint32_t(64 * h + 4 * c + g) * 1024;
+      };
+      float wa[NW], wb[NW];  // weights of the first and the second item, per head block
+      float lse_out = 0.0f;
 #pragma unroll
-      for (int r0 = 0; r0 < 64; r0 += kRound) {
-        const int n = (64 - r0) < kRound ? (64 - r0) : kRound;
+      for (int r0 = 0; r0 < kBlocks; r0 += kRound) {
+        const int n = (kBlocks - r0) < kRound ? (kBlocks - r0) : kRound;
+        asm volatile("" ::: "memory");  // the previous round's LDS reads stay above
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
-          if (j < n) dma16_buffer(pr, uint32_t(r0 + j) * 1024 + lane_off, mb + j * 1024);
+          if (j < n) dma16_buffer(pr, blk_off(r0 + j), mb + j * 1024);
+        if (r0 == 0) {
+          float lo[NW];
+#pragma unroll
+          for (int h = 0; h < NW; ++h)
+            lo[h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                plse_r, uint32_t(other * HP + h * 32 + hl_e) * 4, 0, kSc1));
+#pragma unroll
+          for (int h = 0; h < NW; ++h) {
+            const float lown = x_lse[h * 32 + hl_e];
+            const float l0 = own_first ? lown : lo[h], l1 = own_first ? lo[h] : lown;
+            const float mlse = fmaxf(l0, l1);
+            const float e0 = __builtin_amdgcn_exp2f(l0 - mlse), e1 = __builtin_amdgcn_exp2f(l1 - mlse);
+            const float lam = e0 + e1;
+            const float rl = 1.0f / lam;
+            wa[h] = e0 * rl;
+            wb[h] = e1 * rl;
+            if (h == w) lse_out = (mlse + log2f(lam)) * kLn2;
+          }
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // LDS reads are not moved above earlier buffer stores either: read a
-        // group of blocks, then combine and store them.
+        // LDS reads are not moved above earlier buffer stores: read a group
+        // of blocks, then combine and store them.
         constexpr int kGroup = 6;
 #pragma unroll
-        for (int j0 = 0; j0 < kRound; j0 += kGroup) {
+        for (int jg = 0; jg < kRound; jg += kGroup) {
           f32x4 xs[kGroup];
 #pragma unroll
           for (int jj = 0; jj < kGroup; ++jj)
-            if (j0 + jj < n) xs[jj] = *(const f32x4 LDS_AS*)(mb + (j0 + jj) * 1024 + lane_off);
+            if (jg + jj < n) xs[jj] = *(const f32x4 LDS_AS*)(mb + (jg + jj) * 1024 + lane_e * 16);
 #pragma unroll
           for (int jj = 0; jj < kGroup; ++jj) {
-            if (j0 + jj < n) {
-              const int blk = r0 + j0 + jj, cb = blk >> 2, g = blk & 3;
+            if (jg + jj < n) {
+              const int j = r0 + jg + jj;
+              const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
               float v[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const float own = o[cb][4 * g + r] * own_inv;
-                v[r] = own_first ? fmaf(w1, xs[jj][r], w0 * own) : fmaf(w1, own, w0 * xs[jj][r]);
+                const float own = o[h * CPW + c][4 * g + r] * inv[h];
+                v[r] = own_first ? fmaf(wb[h], xs[jj][r], wa[h] * own) : fmaf(wb[h], own, wa[h] * xs[jj][r]);
               }
-              if (head_ok) store_out4(cb, g, v);
+              store_out4(h, c, g, v);
             }
           }
         }
       }
-      if (head_ok && hi_e == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, head_e * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_out), lse_r, head_e * 4, 0, 0);
     }
+    __syncthreads();
   }
 
   // ---- merge units ----
@@ -778,34 +991,30 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   const int n_units = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.hdr)[5]);
   for (;;) {
     if (n_units == 0) break;
-    if (threadIdx.x == 0) s_item = atomicAdd(&a.hdr[6], 1);
+    if (w == 0) {
+      const int f = lane0_fetch_add(&a.hdr[6], 1);
+      *s_item = f;
+    }
     __syncthreads();
-    const int u = __builtin_amdgcn_readfirstlane(s_item);
+    const int u = __builtin_amdgcn_readfirstlane(*s_item);
     __syncthreads();
     if (u >= n_units) {
-      if (threadIdx.x == 0 && u == n_units + int(gridDim.x) - 1) atomicExch(&a.hdr[6], 0);
+      if (w == 0 && u == n_units + int(gridDim.x) - 1)
+        __hip_atomic_store(&a.hdr[6], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     const int b = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.big)[u / kUnits]);
     const int cb0 = (u % kUnits) * kCb;
     const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
     const int cnt = __builtin_amdgcn_readfirstlane(rq[3]);
-    if (threadIdx.x == 0) {
-      for (int spin = 0;; ++spin) {
-        if (__hip_atomic_load(&a.ctr[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cnt) break;
-        if (spin >= kMergeSpinLimit) {
-          atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
+    if (w == 0) {
+      wave_poll(&a.ctr[kCtr * b + kPublished], cnt, &a.hdr[2], MLA_CHECK_MERGE_WAIT);
     }
     __syncthreads();
     int lane_m = lane;
     asm volatile("" : "+v"(lane_m));
     const int head_m = w * 32 + (lane_m & 31);
     const int hi_m = lane_m >> 5;
-    const bool ok_m = head_m < a.H;
     const uint32_t moff = uint32_t(lane_m) * 16 + uint32_t(cb0) * 4096;
     auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
@@ -868,7 +1077,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(wt[j], x[j][g][r], acc[g][r]);
     }
-    if (ok_m) {
+    {
+      // stores of heads >= H fall outside the resources
       const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
       // block g = 4 c + gg holds columns 32 (cb0 + c) + 8 gg + 4 hi .. +3
@@ -881,7 +1091,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
                                               ooff + (32 * (g >> 2) + 8 * (g & 3)) * 2, 0, 0);
       }
-      if (cb0 == 0 && hi_m == 0) {
+      if (cb0 == 0) {
         const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r,
@@ -890,11 +1100,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     }
     // the request's last unit leaves its counters ready for the next call
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const int t = __hip_atomic_fetch_add(&a.ctr[2 * b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (w == 0) {
+      const int t = lane0_fetch_add(&a.ctr[kCtr * b + kTicket], 1);
       if (t == kUnits - 1) {
-        __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ctr[kCtr * b + kTicket], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ctr[kCtr * b + kPublished], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -939,25 +1149,10 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
   auto pair_sum = [&](float x) {
     return x + __int_as_float(__builtin_amdgcn_ds_bpermute(xlane, __float_as_int(x)));
   };
-  // one atomic per wave, result broadcast from lane 0
-  auto wave_fetch_add = [&](int32_t* p) {
-    int v = 0;
-    if (lane == 0) v = __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  // lane 0 polls a counter until it reaches `target` (bounded)
-  auto wave_wait = [&](int32_t* p, int target) {
-    if (lane == 0) {
-      for (int spin = 0;; ++spin) {
-        if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
-        if (spin >= kMergeSpinLimit) {
-          atomicOr(&a.hdr[2], MLA_CHECK_MERGE_WAIT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-  };
+  // one atomic per wave (lane 0), the old value in every lane
+  auto wave_fetch_add = [&](int32_t* p) { return lane0_fetch_add(p, 1); };
+  // the wave polls a counter until it reaches `target` (bounded)
+  auto wave_wait = [&](int32_t* p, int target) { wave_poll(p, target, &a.hdr[2], MLA_CHECK_MERGE_WAIT); };
 
   // operand read offsets, as in the wide kernel
   int qk_off[8];
@@ -1004,7 +1199,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
       if (n_items <= n_workers) break;
       const int v = wave_fetch_add(&a.hdr[3]);
       if (v + n_workers >= n_items) {
-        if (lane == 0 && v == n_items - 1) atomicExch(&a.hdr[3], 0);
+        if (v == n_items - 1) __hip_atomic_store(&a.hdr[3], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       it = v + n_workers;
@@ -1033,15 +1228,14 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
                                             out_off + (32 * cb + 8 * g) * 2, 0, 0);
     };
     if (t1 <= t0) {
-      // a request with no cached tokens: out = 0, lse = -inf
-      if (head_ok) {
-        const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      // a request with no cached tokens: out = 0, lse = -inf (stores of
+      // heads >= H fall outside the resources)
+      const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) store_out4(cb, g, z);
-        if (hi_e == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), lse_r, hl_e * 4, 0, 0);
-      }
+        for (int g = 0; g < 4; ++g) store_out4(cb, g, z);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-INFINITY), lse_r, hl_e * 4, 0, 0);
       continue;
     }
     const int nst = (t1 - t0 + kSub - 1) / kSub;
@@ -1050,6 +1244,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
     float m_run = -INFINITY, amax = -INFINITY, la = 0.0f, lb = 0.0f;
+    bool first_pass = true;  // uniform: false on a redo
     uint32_t lane16 = uint32_t(lane) * 16;
     asm volatile("" : "+v"(lane16));
     for (;;) {
@@ -1089,11 +1284,11 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
         {
           // register v holds token 4hi + 8(v/4) + (v%4) of the stage
           const int lim = t1 - (t0 + st * kSub) - 4 * hi;
-          if (m_run == -INFINITY) {
+          if (first_pass && st == 0) {
             float mx = -INFINITY;
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              if (8 * (v >> 2) + (v & 3) < lim) mx = fmaxf(mx, sacc[v] * c2);
+              mx = fmaxf(mx, (8 * (v >> 2) + (v & 3) < lim) ? sacc[v] * c2 : -INFINITY);
             m_run = pair_max(mx);
           }
 #pragma unroll
@@ -1113,13 +1308,14 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
           for (int s = 0; s < PFV; ++s) MLA_VREAD(slot, s, vf[s]);
 #pragma unroll
           for (int s = 0; s < 32; ++s) {
-            pv_mfma(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
+            pv_mfma_v(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
             if (s + PFV < 32) MLA_VREAD(slot, s + PFV, vf[s % PFV]);
           }
         }
       }
       if (__ballot(amax > kRefHeadroom) == 0) break;
       m_run += pair_max(amax);
+      first_pass = false;
       amax = -INFINITY;
       la = 0.0f;
       lb = 0.0f;
@@ -1128,28 +1324,26 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
       for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
     }
     pv_drain(o);
-    if (bad) atomicOr(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
+    if (__builtin_amdgcn_readfirstlane(bad)) lane0_atomic_or(&a.hdr[2], MLA_CHECK_BLOCK_ID_RANGE);
 
     const float l_tot = pair_sum(la + lb);
     const float lse2 = m_run + log2f(l_tot);
     const float own_inv = 1.0f / l_tot;
     if (cnt == 1) {
-      if (head_ok) {
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float v[4];
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * g + r] * own_inv;
-            store_out4(cb, g, v);
-          }
-        if (hi_e == 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2), lse_r, hl_e * 4, 0, 0);
-      }
+          for (int r = 0; r < 4; ++r) v[r] = o[cb][4 * g + r] * own_inv;
+          store_out4(cb, g, v);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2 * kLn2), lse_r, hl_e * 4, 0, 0);
       continue;
     }
     // split request: partial in the accumulator layout (lanes of padding
-    // heads store nothing)
+    // heads store values that no merge uses)
     auto part_rsrc = [&](int sl) {
       return __builtin_amdgcn_make_buffer_rsrc((void*)(a.part_o + size_t(sl) * HP * kDV), (short)0,
                                                HP * kDV * 4, 0x00020000);
@@ -1158,40 +1352,34 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
     const uint32_t lane_off = uint32_t(lane_e) * 16;
     auto publish = [&]() {
-      if (head_ok) {
-        const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
+      const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
-        for (int cb = 0; cb < 16; ++cb)
+      for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v4;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
-            __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
-          }
-        if (hi_e == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r,
-                                                uint32_t(it * HP + hl_e) * 4, 0, kSc1);
-      }
+          for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
+          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + hl_e) * 4, 0, kSc1);
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is out
-      if (lane == 0) __hip_atomic_fetch_add(&a.ctr[2 * b + 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lane0_fetch_add(&a.ctr[kCtr * b + kPublished], 1);
     };
     if (cnt >= kMergeMinItems) {
       publish();
       continue;
     }
-    const int ticket = wave_fetch_add(&a.ctr[2 * b]);
+    const int ticket = wave_fetch_add(&a.ctr[kCtr * b + kTicket]);
     if (ticket == 0) {
       publish();
       continue;
     }
     // the last of two: its partner took its ticket earlier and only has
     // stores left
-    wave_wait(&a.ctr[2 * b + 1], 1);
-    if (lane == 0) {
-      __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    wave_wait(&a.ctr[kCtr * b + kPublished], 1);
+    __hip_atomic_store(&a.ctr[kCtr * b + kTicket], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.ctr[kCtr * b + kPublished], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
       const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
       auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
@@ -1236,15 +1424,14 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
                 const float own = o[cb][4 * g + r] * own_inv;
                 v[r] = own_first ? fmaf(w1, xs[jj][r], w0 * own) : fmaf(w1, own, w0 * xs[jj][r]);
               }
-              if (head_ok) store_out4(cb, g, v);
+              store_out4(cb, g, v);
             }
           }
         }
         // this round's reads are done before the next round refills the slot
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      if (head_ok && hi_e == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, hl_e * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r, hl_e * 4, 0, 0);
     }
   }
 #undef MLA_KREAD
@@ -1255,19 +1442,18 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     if (n_units == 0) break;
     const int u = wave_fetch_add(&a.hdr[6]);
     if (u >= n_units) {
-      if (lane == 0 && u == n_units + n_workers - 1) atomicExch(&a.hdr[6], 0);
+      if (u == n_units + n_workers - 1) __hip_atomic_store(&a.hdr[6], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     const int b = __builtin_amdgcn_readfirstlane(((const CONST_AS int32_t*)a.big)[u / kNarrowUnits]);
     const int cb0 = (u % kNarrowUnits) * (16 / kNarrowUnits);
     const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
     const int cnt = __builtin_amdgcn_readfirstlane(rq[3]);
-    wave_wait(&a.ctr[2 * b + 1], cnt);
+    wave_wait(&a.ctr[kCtr * b + kPublished], cnt);
     int lane_m = lane;
     asm volatile("" : "+v"(lane_m));
     const int hl_m = lane_m & 31;
     const int hi_m = lane_m >> 5;
-    const bool ok_m = hl_m < a.H;
     const uint32_t moff = uint32_t(lane_m) * 16 + uint32_t(cb0) * 4096;
     auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
@@ -1330,7 +1516,8 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(wt[j], x[j][g][r], acc[g][r]);
     }
-    if (ok_m) {
+    {
+      // stores of heads >= H fall outside the resources
       const __amdgpu_buffer_rsrc_t out_r = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.out + size_t(b) * a.H * kDV), (short)0, a.H * kDV * 2, 0x00020000);
       const uint32_t ooff = uint32_t(hl_m * kDV + 4 * hi_m + 32 * cb0) * 2;
@@ -1342,7 +1529,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), out_r,
                                               ooff + (32 * (g >> 2) + 8 * (g & 3)) * 2, 0, 0);
       }
-      if (cb0 == 0 && hi_m == 0) {
+      if (cb0 == 0) {
         const __amdgpu_buffer_rsrc_t lse_r = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.lse + size_t(b) * a.H), (short)0, a.H * 4, 0x00020000);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((mlse + log2f(lam)) * kLn2), lse_r,
@@ -1350,10 +1537,10 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
       }
     }
     // the request's last unit leaves its counters ready for the next call
-    const int t = wave_fetch_add(&a.ctr[2 * b]);
-    if (lane == 0 && t == kNarrowUnits - 1) {
-      __hip_atomic_store(&a.ctr[2 * b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[2 * b + 1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int t = wave_fetch_add(&a.ctr[kCtr * b + kTicket]);
+    if (t == kNarrowUnits - 1) {
+      __hip_atomic_store(&a.ctr[kCtr * b + kTicket], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ctr[kCtr * b + kPublished], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1483,8 +1670,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     nf_loc += L / chunk;
     nr_loc += (L % chunk) ? 1 : 0;
     ne_loc += (L == 0) ? 1 : 0;
-    ctr[2 * b] = 0;
-    ctr[2 * b + 1] = 0;
+#pragma unroll
+    for (int k = 0; k < kCtr; ++k) ctr[kCtr * b + k] = 0;
   }
   const int NF = block_scan(nf_loc, s_scan).y;
   const int NR = block_scan(nr_loc, s_scan).y;
@@ -1597,7 +1784,11 @@ int item_overhead_tokens(int H) { return 32 + 2 * H; }
 
 template <int NW, int NS>
 hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((mla_attend_kernel<NW, NS>), dim3(grid), dim3(NW * 64), 0, st, a);
+  // block sizes of 32 tokens or more keep every stage in one block
+  if (a.lgBS >= 5)
+    hipLaunchKernelGGL((mla_attend_kernel<NW, NS, true>), dim3(grid), dim3(NW * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((mla_attend_kernel<NW, NS, false>), dim3(grid), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
