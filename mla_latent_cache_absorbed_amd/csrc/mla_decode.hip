@@ -847,8 +847,13 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
-    // this lane's 16 bytes of block (h, CPW w + c, g): slab + (64 h + 4 c + g) KB
+    // this lane's 16 bytes of block (h, CPW w + c, g): slab + (64 h + 4 c + g)
+    // KB; pad[h] moves the lanes of padding heads past the resource, so their
+    // stores and loads are dropped without a branch
     const uint32_t slab = uint32_t(4 * CPW * w) * 1024 + uint32_t(lane_e) * 16;
+    uint32_t pad[NW];
+#pragma unroll
+    for (int h = 0; h < NW; ++h) pad[h] = (h * 32 + hl_e < a.H) ? 0u : 0x40000000u;
     auto publish = [&]() {
       const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
@@ -860,7 +865,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
             f32x4 v4;
 #pragma unroll
             for (int r = 0; r < 4; ++r) v4[r] = o[h * CPW + c][4 * g + r] * inv[h];
-            __builtin_amdgcn_raw_buffer_store_b128(v4, pr, slab + (64 * h + 4 * c + g) * 1024, 0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b128(v4, pr, slab + pad[h] + (64 * h + 4 * c + g) * 1024, 0, kSc1);
           }
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's partial is out
@@ -916,7 +921,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       constexpr int kBlocks = NW * CPW * 4;       // 64 blocks per wave
       auto blk_off = [&](int j) {  // block j = (h, c, g) of this wave's slab
         const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
-        return slab + uint32_t(64 * h + 4 * c + g) * 1024;
+        return slab + pad[h] + uint32_t(64 * h + 4 * c + g) * 1024;
       };
       float wa[NW], wb[NW];  // weights of the first and the second item, per head block
       float lse_out = 0.0f;
@@ -1015,7 +1020,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     asm volatile("" : "+v"(lane_m));
     const int head_m = w * 32 + (lane_m & 31);
     const int hi_m = lane_m >> 5;
-    const uint32_t moff = uint32_t(lane_m) * 16 + uint32_t(cb0) * 4096;
+    // lanes of padding heads read past the resource (zeros, no traffic)
+    const uint32_t moff = (head_m < a.H ? uint32_t(lane_m) * 16 : 0x40000000u) + uint32_t(cb0) * 4096;
     auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
@@ -1127,6 +1133,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 constexpr int kNarrowWaves = 4;
 constexpr int kNarrowUnits = 4;  // merge units per widely split request
 
+template <bool kOne>  // as for the wide kernel: every stage lies in one block
 __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNarrowWaves * kStageBytes];
   constexpr int PFK = 4;  // score operand reads in flight
@@ -1246,7 +1253,9 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     float m_run = -INFINITY, amax = -INFINITY, la = 0.0f, lb = 0.0f;
     bool first_pass = true;  // uniform: false on a redo
     uint32_t lane16 = uint32_t(lane) * 16;
-    asm volatile("" : "+v"(lane16));
+    uint32_t rb_tok = ((lane16 >> 4) & 31) * (kD * 2);
+    uint32_t rb_cp = 1024 + (lane16 >> 9) * 16;
+    asm volatile("" : "+v"(lane16), "+v"(rb_tok), "+v"(rb_cp));
     for (;;) {
       // fixed exponent reference from the item's first stage, with a redo if
       // a later score exceeds it by more than the headroom (as in the wide
@@ -1261,11 +1270,18 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
         for (int s = 0; s < 36; ++s) qreg[s] = qp[2 * s];
       }
       for (int st = 0; st < nst; ++st) {
-        const StageIds id = stage_ids(a, b, t0 + st * kSub, t1, bad);
         // this wave's reads of the slot are done before it is refilled
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if constexpr (kOne) {
+          const StageOne id = stage_one(a, b, t0 + st * kSub, t1, bad);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 36; ++j) issue_load<1>(a, id, slot, t1, 0, lane16, j);
+          for (int j = 0; j < 36; ++j) issue_one<1>(id, slot, 0, lane16, rb_tok, rb_cp, j);
+        } else {
+          const StageIds id = stage_ids(a, b, t0 + st * kSub, t1, bad);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int j = 0; j < 36; ++j) issue_load<1>(a, id, slot, t1, 0, lane16, j);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         f32x16 sacc;
         {
@@ -1351,6 +1367,9 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
     const uint32_t lane_off = uint32_t(lane_e) * 16;
+    // partial offset of this lane: lanes of padding heads point past the
+    // resource, so their stores and loads are dropped without a branch
+    const uint32_t part_off = hl_e < a.H ? lane_off : 0x40000000u;
     auto publish = [&]() {
       const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
@@ -1360,7 +1379,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
           f32x4 v4;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v4[r] = o[cb][4 * g + r] * own_inv;
-          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + lane_off, 0, kSc1);
+          __builtin_amdgcn_raw_buffer_store_b128(v4, pr, (cb * 4 + g) * 1024 + part_off, 0, kSc1);
         }
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + hl_e) * 4, 0, kSc1);
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the partial is out
@@ -1405,7 +1424,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
         const int n = (64 - r0) < kRound ? (64 - r0) : kRound;
 #pragma unroll
         for (int j = 0; j < kRound; ++j)
-          if (j < n) dma16_buffer(pr, uint32_t(r0 + j) * 1024 + lane_off, slot + j * 1024);
+          if (j < n) dma16_buffer(pr, uint32_t(r0 + j) * 1024 + part_off, slot + j * 1024);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         constexpr int kGroup = 6;
 #pragma unroll
@@ -1454,7 +1473,8 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     asm volatile("" : "+v"(lane_m));
     const int hl_m = lane_m & 31;
     const int hi_m = lane_m >> 5;
-    const uint32_t moff = uint32_t(lane_m) * 16 + uint32_t(cb0) * 4096;
+    // lanes of padding heads read past the resource (zeros, no traffic)
+    const uint32_t moff = (hl_m < a.H ? uint32_t(lane_m) * 16 : 0x40000000u) + uint32_t(cb0) * 4096;
     auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
@@ -1892,7 +1912,10 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
     case 4: e = launch_attend<4, 4>(a, grid, st); break;
     case 2: e = launch_attend<2, 4>(a, grid, st); break;
     default:
-      hipLaunchKernelGGL(mla_attend_narrow_kernel, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
+      if (a.lgBS >= 5)
+        hipLaunchKernelGGL(mla_attend_narrow_kernel<true>, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL(mla_attend_narrow_kernel<false>, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
       e = hipGetLastError();
       break;
   }
