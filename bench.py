@@ -114,6 +114,40 @@ def cpu_baseline(w, budget_s: float):
                       f"{done_tokens} tokens x {w.H} heads), float64 NumPy, {elapsed:.1f} s"}
 
 
+def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
+    """Peaks this box attains with plain library kernels, timed with events: a
+    device-to-device copy of 2 GiB (reads and writes counted) and a bf16 GEMM
+    (8192^3 on hipBLASLt).  The attend kernel's rates are also given as
+    fractions of them."""
+    import torch
+    dev = torch.device("cuda")
+    x = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16).contiguous()
+    bm = torch.randn(8192, 8192, device=dev).to(torch.bfloat16).contiguous()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    t_cp = timed(lambda: y.copy_(x), 10)
+    t_mm = timed(lambda: torch.mm(a, bm), 10)
+    cp_gbs = 2 * x.numel() / t_cp / 1e9
+    mm_tfs = 2 * 8192 ** 3 / t_mm / 1e12
+    del x, y, a, bm
+    return {"copy_read_write_gbs": cp_gbs, "bf16_gemm_tflops": mm_tfs,
+            "attend_frac_of_copy": achieved_gbs / cp_gbs,
+            "attend_frac_of_gemm": tflops / mm_tfs}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -187,6 +221,7 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
     attend_ms = [a.elapsed_time(b) for a, b in pairs]
     attend_avg_ms = sum(attend_ms) / len(attend_ms)
+    attend_sorted = sorted(attend_ms)
     hdr = ws.header()
 
     tokens_step = acc.token_reads(seq, layers)
@@ -227,6 +262,8 @@ def main():
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": hbm_traffic_record(name),
             "launch_ms": attend_avg_ms,
+            "launch_ms_median": attend_sorted[len(attend_sorted) // 2],
+            "launch_ms_min": attend_sorted[0],
             "algorithmic_bytes_per_launch": alg_bytes,
             "mfma_tflops": tflops,
             "mfma_frac": tflops / MFMA_BF16_PEAK_TFS,
@@ -234,6 +271,7 @@ def main():
         },
         "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
     }
+    rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
