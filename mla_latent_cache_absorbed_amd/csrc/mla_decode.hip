@@ -1579,42 +1579,86 @@ __device__ __forceinline__ int plan_candidate(int i) {
   return 32 * int(k);
 }
 
-// Inclusive block-wide scan of one int per thread; returns (inclusive, total).
-// A 64-lane shuffle scan in each wave, then the four wave totals through LDS.
-__device__ __forceinline__ int2 block_scan(int v, int* s_scan) {
+// Inclusive block-wide scan of four ints per thread; returns the inclusive
+// scan and the block totals.  A 64-lane shuffle scan in each wave, then the
+// four wave totals through LDS.
+struct Scan4 {
+  int4 incl, total;
+};
+__device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  int x = v;
+  int4 x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+    const int y0 = __shfl_up(x.x, off, 64), y1 = __shfl_up(x.y, off, 64);
+    const int y2 = __shfl_up(x.z, off, 64), y3 = __shfl_up(x.w, off, 64);
+    if (lane >= off) {
+      x.x += y0;
+      x.y += y1;
+      x.z += y2;
+      x.w += y3;
+    }
   }
   if (lane == 63) s_scan[wv] = x;
   __syncthreads();
-  int pre = 0, tot = 0;
+  int4 pre = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < kPlanThreads / 64; ++i) {
-    const int t = s_scan[i];
-    pre += (i < wv) ? t : 0;
-    tot += t;
+    const int4 t = s_scan[i];
+    if (i < wv) {
+      pre.x += t.x;
+      pre.y += t.y;
+      pre.z += t.z;
+      pre.w += t.w;
+    }
+    tot.x += t.x;
+    tot.y += t.y;
+    tot.z += t.z;
+    tot.w += t.w;
   }
   __syncthreads();
-  return make_int2(x + pre, tot);
+  Scan4 r;
+  r.incl = make_int4(x.x + pre.x, x.y + pre.y, x.z + pre.z, x.w + pre.w);
+  r.total = tot;
+  return r;
 }
 
 // Items are laid out full chunks first, then the last (shorter) chunk of each
-// request, then one item per empty request.
+// request, then one item per empty request.  With at most kPlanLens requests
+// the (clamped) lengths are read from memory once and kept in LDS.
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
     int ovh, int cap, int units_per_req, int32_t* __restrict__ hdr, int4* __restrict__ req,
     int32_t* __restrict__ ctr, int32_t* __restrict__ big, int4* __restrict__ items) {
-  __shared__ long long s_cost[kPlanThreads];
-  __shared__ int s_chunk[kPlanThreads];
-  __shared__ int s_scan[kPlanThreads];
+  __shared__ long long s_cost[kPlanThreads / 64];
+  __shared__ int s_chunk[kPlanThreads / 64];
+  __shared__ int4 s_scan[kPlanThreads / 64];
   __shared__ __attribute__((aligned(16))) int s_len[kPlanLens];
   const int tid = threadIdx.x;
   const int Lmax = M << lgBS;
+  const bool resident = B <= kPlanLens;
+  auto clamp_len = [&](int L0) { return min(max(L0, 0), Lmax); };
+  // lengths of requests b0 .. b0 + nb - 1 into LDS, padded with -1 to a
+  // multiple of 4; returns this thread's range-check bit
+  auto stage = [&](int b0, int nb) {
+    int bad = 0;
+    const int nb4 = (nb + 3) & ~3;
+    for (int i = tid; i < nb4; i += kPlanThreads) {
+      int L = -1;
+      if (i < nb) {
+        const int L0 = seq_lens[b0 + i];
+        bad |= (L0 < 0 || L0 > Lmax) ? 1 : 0;
+        L = clamp_len(L0);
+      }
+      s_len[i] = L;
+    }
+    __syncthreads();
+    return bad;
+  };
+  int bad = 0;
+  if (resident) bad = stage(0, B);
+  auto len_of = [&](int b) { return resident ? s_len[b] : clamp_len(seq_lens[b]); };
 
   // 1) chunk size: each thread prices one candidate,
   //    cost = ceil(items / slots) * (chunk + per-item overhead).
@@ -1626,27 +1670,25 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     // correction; this keeps integer division out of the B x 256 loop.
     const int d = T >> 5;
     const float inv_d = 1.0f / float(d);
+    auto items_of = [&](int L) {
+      const int m = (L + 31) >> 5;
+      int q = int(float(m) * inv_d);
+      const int r = m - q * d;
+      q += (r >= d) - (r < 0);
+      const int rr = m - q * d;
+      return (L < 0) ? 0 : max(1, q + (rr > 0));  // L < 0: padding
+    };
     long long n = 0;
     for (int b0 = 0; b0 < B; b0 += kPlanLens) {
       const int nb = min(kPlanLens, B - b0);
-      // lengths in 32-token units, padded to a multiple of 4 with zeros
+      if (!resident) bad |= stage(b0, nb);
       const int nb4 = (nb + 3) & ~3;
-      for (int i = tid; i < nb4; i += kPlanThreads)
-        s_len[i] = (i < nb) ? (min(max(seq_lens[b0 + i], 0), Lmax) + 31) >> 5 : -1;
-      __syncthreads();
-      auto items_of = [&](int m) {
-        int q = int(float(m) * inv_d);
-        const int r = m - q * d;
-        q += (r >= d) - (r < 0);
-        const int rr = m - q * d;
-        return (m < 0) ? 0 : max(1, q + (rr > 0));  // m < 0: padding
-      };
 #pragma unroll 4
       for (int i = 0; i < nb4; i += 4) {
         const int4 m4 = *reinterpret_cast<const int4*>(&s_len[i]);
         n += items_of(m4.x) + items_of(m4.y) + items_of(m4.z) + items_of(m4.w);
       }
-      __syncthreads();
+      if (!resident) __syncthreads();
     }
     // cheapest candidate, the larger chunk on ties: a shuffle reduction in
     // each wave, then over the four waves
@@ -1678,54 +1720,52 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     chunk = kb;
     // no candidate fits the workspace: one item per request
     if (cb >= (1ll << 62)) chunk = ((Lmax + 31) / 32) * 32;
-    __syncthreads();
+  } else if (!resident) {
+    for (int b0 = 0; b0 < B; b0 += kPlanLens) {
+      bad |= stage(b0, min(kPlanLens, B - b0));
+      __syncthreads();
+    }
   }
 
-  // 2) totals: full chunks, remainders, empty requests
-  int nf_loc = 0, nr_loc = 0, ne_loc = 0, bad = 0;
+  // 2) totals: full chunks, remainders, empty requests, range-check bits;
+  //    the counters of every request start at 0
+  int4 loc = make_int4(0, 0, 0, bad);
   for (int b = tid; b < B; b += kPlanThreads) {
-    const int L0 = seq_lens[b];
-    if (L0 < 0 || L0 > Lmax) bad = 1;
-    const int L = min(max(L0, 0), Lmax);
-    nf_loc += L / chunk;
-    nr_loc += (L % chunk) ? 1 : 0;
-    ne_loc += (L == 0) ? 1 : 0;
+    const int L = len_of(b);
+    loc.x += L / chunk;
+    loc.y += (L % chunk) ? 1 : 0;
+    loc.z += (L == 0) ? 1 : 0;
 #pragma unroll
     for (int k = 0; k < kCtr; ++k) ctr[kCtr * b + k] = 0;
   }
-  const int NF = block_scan(nf_loc, s_scan).y;
-  const int NR = block_scan(nr_loc, s_scan).y;
-  const int NE = block_scan(ne_loc, s_scan).y;
-  const int any_bad = block_scan(bad, s_scan).y;
+  const int4 tot = block_scan4(loc, s_scan).total;
+  const int NF = tot.x, NR = tot.y, NE = tot.z, any_bad = tot.w;
 
   // 3) per-request placement from exclusive scans; requests split into
   //    kMergeMinItems or more items are listed for the merge units
-  int carry_f = 0, carry_r = 0, carry_e = 0, carry_b = 0;
+  int4 carry = make_int4(0, 0, 0, 0);
   for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
     const int b = b0 + tid;
-    const int L = (b < B) ? min(max(seq_lens[b], 0), Lmax) : 0;
+    const int L = (b < B) ? len_of(b) : 0;
     const int nf = L / chunk;
     const int nr = (L % chunk) ? 1 : 0;
     const int ne = (b < B && L == 0) ? 1 : 0;
     const int cnt = nf + nr;
     const int nbg = (b < B && cnt >= kMergeMinItems) ? 1 : 0;
-    const int2 fs = block_scan(nf, s_scan);
-    const int2 rs = block_scan(nr, s_scan);
-    const int2 es = block_scan(ne, s_scan);
-    const int2 bs = block_scan(nbg, s_scan);
+    const Scan4 sc = block_scan4(make_int4(nf, nr, ne, nbg), s_scan);
     if (b < B) {
-      const int fbeg = carry_f + fs.x - nf;
-      const int ritem = nr ? (NF + carry_r + rs.x - nr) : -1;
+      const int fbeg = carry.x + sc.incl.x - nf;
+      const int ritem = nr ? (NF + carry.y + sc.incl.y - nr) : -1;
       req[b] = make_int4(fbeg, nf, ritem, cnt);
       for (int s = 0; s < nf; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
       if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt);
-      if (ne) items[NF + NR + carry_e + es.x - 1] = make_int4(b, 0, 0, 0);
-      if (nbg) big[carry_b + bs.x - 1] = b;
+      if (ne) items[NF + NR + carry.z + sc.incl.z - 1] = make_int4(b, 0, 0, 0);
+      if (nbg) big[carry.w + sc.incl.w - 1] = b;
     }
-    carry_f += fs.y;
-    carry_r += rs.y;
-    carry_e += es.y;
-    carry_b += bs.y;
+    carry.x += sc.total.x;
+    carry.y += sc.total.y;
+    carry.z += sc.total.z;
+    carry.w += sc.total.w;
   }
 
   // 4) header
@@ -1735,7 +1775,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     hdr[2] = any_bad ? MLA_CHECK_SEQ_LEN_RANGE : 0;
     hdr[3] = 0;
     hdr[4] = NF;
-    hdr[5] = carry_b * units_per_req;
+    hdr[5] = carry.w * units_per_req;
     hdr[6] = 0;
   }
 }

@@ -112,6 +112,40 @@ def test_forced_splits(H, chunk):
     assert np.array_equal(lse2.cpu().numpy(), lse)
 
 
+def test_more_requests_than_the_plan_stages():
+    """B > 4096: the plan reads lengths from memory in passes instead of
+    keeping them in LDS (auto and forced chunk sizes), with empty, short and a
+    few long requests."""
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 25, size=4500).tolist()
+    for i in (7, 2222, 4499):
+        lens[i] = 1500
+    w = _to_gpu(wl.make_custom(lens, H=16, BS=16, seed=5, poison_unused=True))
+    # sampled requests (the long ones, some empty ones, others at random),
+    # each decoded by the oracle over its own pages
+    empty = [i for i, L in enumerate(lens) if L == 0][:20]
+    reqs = sorted(set([7, 2222, 4499, 0, 4095, 4096, 4097] + empty +
+                      rng.choice(4500, size=150, replace=False).tolist()))
+    qb = wl.bf16_bits(w.q.cpu())
+    bt = w.block_table.cpu()
+    ro, rl = [], []
+    for b in reqs:
+        nblk = -(-lens[b] // w.BS)
+        sub = wl.bf16_bits(w.cache[bt[b, :nblk].long().to(w.cache.device)].cpu())
+        o, l = orc.oracle_decode(qb[b:b + 1], sub, np.arange(max(nblk, 1), dtype=np.int64)[None],
+                                 np.array([lens[b]]), w.scale)
+        ro.append(o[0])
+        rl.append(l[0])
+    ro, rl = np.stack(ro), np.stack(rl)
+    # a forced chunk must keep B * ceil(M * BS / chunk) within B + 1024 items
+    for chunk in (None, 1536):
+        ws = mla.Workspace(w.B, w.H, w.M, w.BS)
+        out, lse = _run(w, chunk_tokens=chunk, ws=ws)
+        _assert_parity(out[reqs], lse[reqs], ro, rl, f"B=4500 chunk={chunk} ({len(reqs)} sampled requests)")
+        hdr = ws.header()
+        assert hdr[3] == 0 and hdr[6] == 0 and ws.check_flags() == 0, hdr
+
+
 def test_empty_requests_and_empty_batch():
     lens = [0, 70, 0, 1]
     w = _to_gpu(wl.make_custom(lens, H=128, BS=16, seed=3, poison_unused=True))
