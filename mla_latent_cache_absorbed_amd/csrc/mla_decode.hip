@@ -1635,12 +1635,14 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   __shared__ int s_chunk[kPlanThreads / 64];
   __shared__ int4 s_scan[kPlanThreads / 64];
   __shared__ __attribute__((aligned(16))) int s_len[kPlanLens];
+  __shared__ __attribute__((aligned(16))) float s_m[kPlanLens];
   const int tid = threadIdx.x;
   const int Lmax = M << lgBS;
   const bool resident = B <= kPlanLens;
   auto clamp_len = [&](int L0) { return min(max(L0, 0), Lmax); };
   // lengths of requests b0 .. b0 + nb - 1 into LDS, padded with -1 to a
-  // multiple of 4; returns this thread's range-check bit
+  // multiple of 4, and ceil(L / 32) as floats, padded with 0; returns this
+  // thread's range-check bit
   auto stage = [&](int b0, int nb) {
     int bad = 0;
     const int nb4 = (nb + 3) & ~3;
@@ -1652,6 +1654,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
         L = clamp_len(L0);
       }
       s_len[i] = L;
+      s_m[i] = float((max(L, 0) + 31) >> 5);
     }
     __syncthreads();
     return bad;
@@ -1678,15 +1681,34 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
       const int rr = m - q * d;
       return (L < 0) ? 0 : max(1, q + (rr > 0));  // L < 0: padding
     };
+    // Float form of the same count, four VALU ops per request: with m < 2^22
+    // and 1/d within one ulp, fma(m, 1/d, -1/(2d)) lies within 1/(2d) of
+    // (m - 1/2) / d, so its ceiling is ceil(m / d) exactly.  The float sum is
+    // exact below 2^24 and stays at or above 2^24 (past any workspace cap)
+    // once the count gets there.  Padding entries (m = 0) count one each.
+    const bool fast = Lmax <= (1 << 26);
+    const float inv_df = 1.0f / float(d);
+    const float half_df = 0.5f * inv_df;
+    auto items_f = [&](float m) { return fmaxf(1.0f, ceilf(__builtin_fmaf(m, inv_df, -half_df))); };
     long long n = 0;
     for (int b0 = 0; b0 < B; b0 += kPlanLens) {
       const int nb = min(kPlanLens, B - b0);
       if (!resident) bad |= stage(b0, nb);
       const int nb4 = (nb + 3) & ~3;
+      if (fast) {
+        float acc = 0.0f;
 #pragma unroll 4
-      for (int i = 0; i < nb4; i += 4) {
-        const int4 m4 = *reinterpret_cast<const int4*>(&s_len[i]);
-        n += items_of(m4.x) + items_of(m4.y) + items_of(m4.z) + items_of(m4.w);
+        for (int i = 0; i < nb4; i += 4) {
+          const float4 m4 = *reinterpret_cast<const float4*>(&s_m[i]);
+          acc += (items_f(m4.x) + items_f(m4.y)) + (items_f(m4.z) + items_f(m4.w));
+        }
+        n += (long long)acc - (nb4 - nb);
+      } else {
+#pragma unroll 4
+        for (int i = 0; i < nb4; i += 4) {
+          const int4 m4 = *reinterpret_cast<const int4*>(&s_len[i]);
+          n += items_of(m4.x) + items_of(m4.y) + items_of(m4.z) + items_of(m4.w);
+        }
       }
       if (!resident) __syncthreads();
     }
