@@ -148,6 +148,31 @@ def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
             "attend_frac_of_gemm": tflops / mm_tfs}
 
 
+def append_record(w, reps: int = 200) -> dict:
+    """The paged latent append (the step before decode) on the same cache: one
+    new token per request, written over each request's last cached row after
+    the timed decode steps.  HIP events around `reps` launches."""
+    import torch
+    import mla_latent_cache_absorbed_amd as mla
+    dev = w.q.device
+    g = torch.Generator(device=dev).manual_seed(7)
+    new = torch.randn((w.B, 576), generator=g, device=dev).to(torch.bfloat16)
+    pos = (w.seq_lens - 1).clamp(min=0).to(torch.int32)
+    mla.append_latent(new[:, :512], new[:, 512:], pos, w.block_table, w.cache)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mla.append_latent(new[:, :512], new[:, 512:], pos, w.block_table, w.cache)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    moved = w.B * 576 * 2 * 2  # each row read once and written once
+    return {"kernel": "mla_append_kernel", "rows": w.B, "launch_us": t * 1e6,
+            "gb_s": moved / t / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -271,6 +296,7 @@ def main():
         },
         "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
     }
+    rec["append"] = append_record(w0)
     rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import MlaError  # noqa: F401
 
-__all__ = ["decode", "Workspace", "plan", "attend", "MlaError"]
+__all__ = ["decode", "Workspace", "plan", "attend", "append_latent", "MlaError"]
 
 
 def _stream() -> int:
@@ -112,3 +112,37 @@ def attend(q, latent_cache, block_table, scale, out, lse, workspace: Workspace) 
                                 float(scale), out.data_ptr(), lse.data_ptr(), B, H, NB, BS, M,
                                 workspace.ptr, workspace.nbytes, _stream())
     _lib._check("mla_decode_attend", st)
+
+
+def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Tensor,
+                  block_table: torch.Tensor, latent_cache: torch.Tensor,
+                  skipped: Optional[torch.Tensor] = None) -> None:
+    """Store each request's new token (kv_c [B, >=512], k_rope [B, >=64], bf16 rows
+    with unit inner stride) at its position in the paged latent cache.
+    positions [B] int32 (negative: no token); skipped: optional int32 [1]
+    device counter of requests that could not be written."""
+    if kv_c.dtype != torch.bfloat16 or k_rope.dtype != torch.bfloat16:
+        raise TypeError("kv_c and k_rope must be bfloat16")
+    if latent_cache.dtype != torch.bfloat16 or latent_cache.dim() != 3 or latent_cache.shape[2] != 576:
+        raise ValueError("latent_cache must be bfloat16 [NB, BS, 576]")
+    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise TypeError("positions and block_table must be int32")
+    B = positions.shape[0]
+    if kv_c.dim() != 2 or k_rope.dim() != 2 or kv_c.shape[0] != B or k_rope.shape[0] != B:
+        raise ValueError("kv_c and k_rope must be [B, n] with B = len(positions)")
+    if kv_c.shape[1] < 512 or k_rope.shape[1] < 64 or kv_c.stride(1) != 1 or k_rope.stride(1) != 1:
+        raise ValueError("kv_c rows need 512 and k_rope rows 64 contiguous elements")
+    if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, M] tensor")
+    if not (latent_cache.is_contiguous() and positions.is_contiguous()):
+        raise ValueError("latent_cache and positions must be contiguous")
+    if skipped is not None and (skipped.dtype != torch.int32 or skipped.numel() < 1):
+        raise TypeError("skipped must be an int32 device tensor")
+    NB, BS, _ = latent_cache.shape
+    M = block_table.shape[1]
+    st = _lib.mla_append_latent(kv_c.data_ptr(), kv_c.stride(0), k_rope.data_ptr(), k_rope.stride(0),
+                                positions.data_ptr(), block_table.data_ptr(),
+                                latent_cache.data_ptr(),
+                                skipped.data_ptr() if skipped is not None else None,
+                                B, NB, BS, M, _stream())
+    _lib._check("mla_append_latent", st)

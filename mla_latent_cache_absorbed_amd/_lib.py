@@ -1,4 +1,5 @@
-"""ctypes binding of ``libmla_decode.so`` (C ABI in ``include/mla_decode.h``).
+"""ctypes binding of ``libmla_decode.so`` (C ABI in ``include/mla_decode.h`` and
+``include/mla_append.h``).
 
 Argument marshalling only: every step of the decode runs in the HIP library.
 The library must have been built (``python -m mla_latent_cache_absorbed_amd.build``
@@ -38,6 +39,7 @@ SIGNATURES = {
     "mla_decode_read_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_decode_abi_version": (_I, []),
+    "mla_append_latent": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -107,3 +109,9 @@ def mla_decode_read_error(workspace, stream) -> int:
 
 def mla_decode_abi_version() -> int:
     return int(lib().mla_decode_abi_version())
+
+
+def mla_append_latent(kv_c, kv_c_stride, k_rope, k_rope_stride, positions, block_table,
+                      latent_cache, skipped, B, NB, BS, M, stream) -> int:
+    return lib().mla_append_latent(kv_c, kv_c_stride, k_rope, k_rope_stride, positions,
+                                   block_table, latent_cache, skipped, B, NB, BS, M, stream)

@@ -8,6 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "mla_decode.hip")
+SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_append.hip")]
 LIB = os.path.join(HERE, "libmla_decode.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,7 +28,7 @@ FLAGS = [
 def build(verbose: bool = False, extra=()) -> str:
     """Compile ``libmla_decode.so``; returns its path.  Always recompiles."""
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,7 +42,9 @@ def build(verbose: bool = False, extra=()) -> str:
     # MFMAs issued from inline asm: the compiler cannot see their operand
     # hazards, so the compiled code is checked for them
     from mla_latent_cache_absorbed_amd import isa_check
-    probs = isa_check.check_source(SRC, HIPCC, [*FLAGS, *extra])
+    probs = []
+    for src in SOURCES:
+        probs += isa_check.check_source(src, HIPCC, [*FLAGS, *extra])
     if probs:
         raise RuntimeError("MFMA operand hazards in the compiled code:\n" + "\n".join(probs))
     return LIB

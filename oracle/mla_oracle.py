@@ -198,6 +198,41 @@ def merge_partials(parts: Sequence[Tuple[np.ndarray, np.ndarray]]
 
 
 # ---------------------------------------------------------------------------
+# paged append: the step that puts a new token into the cache
+# ---------------------------------------------------------------------------
+
+def oracle_append(latent_cache: np.ndarray, block_table: np.ndarray,
+                  positions: Sequence[int], kv_c: np.ndarray, k_rope: np.ndarray
+                  ) -> Tuple[np.ndarray, int]:
+    """Cache after storing request b's new token at logical position positions[b].
+
+    The token goes to the row the decode reads it from, block
+    ``block_table[b, p // BS]``, offset ``p % BS`` (page "MLA 的 TP 切分…",
+    section 3.1: per layer one [NB, BS, 576] array, elements 0..511 kv_c and
+    512..575 k_rope).  The stored bits are the inputs' bits.  A negative
+    position means no token; a position at or past ``M * BS`` or a block id
+    outside ``[0, NB)`` is skipped and counted.  Requests are applied in
+    order.  Returns (new cache, number skipped); the input cache is not
+    modified.
+    """
+    cache = np.array(latent_cache, copy=True)
+    NB, BS, _ = cache.shape
+    bt = np.asarray(block_table)
+    M = bt.shape[1]
+    skipped = 0
+    for b, p in enumerate(int(x) for x in positions):
+        if p < 0:
+            continue
+        if p >= M * BS or not 0 <= int(bt[b, p // BS]) < NB:
+            skipped += 1
+            continue
+        row = cache[int(bt[b, p // BS]), p % BS]
+        row[:D_KVC] = kv_c[b][:D_KVC]
+        row[D_KVC:] = k_rope[b][:D_ROPE]
+    return cache, skipped
+
+
+# ---------------------------------------------------------------------------
 # the explicit (non-absorbed) form, for checking the absorbed rewrite
 # ---------------------------------------------------------------------------
 

@@ -9,13 +9,16 @@ import pytest
 from mla_latent_cache_absorbed_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)
     return sorted(set(names))
 
 
@@ -120,6 +123,41 @@ def test_plan_attend_reject_bad_arguments_on_host(L):
         == _lib.MLA_ERR_WORKSPACE
     assert _lib.lib().mla_decode_read_error(None, ctypes.byref(ctypes.c_int32()), None) \
         == _lib.MLA_ERR_NULL_POINTER
+
+
+def _append(**kw):
+    a = dict(kv=FAKE, kvs=576, kr=FAKE + 1024, krs=576, pos=FAKE, table=FAKE, cache=FAKE,
+             skipped=None, B=4, NB=14, BS=16, M=7, stream=None)
+    a.update(kw)
+    return _lib.mla_append_latent(a["kv"], a["kvs"], a["kr"], a["krs"], a["pos"], a["table"],
+                                  a["cache"], a["skipped"], a["B"], a["NB"], a["BS"], a["M"],
+                                  a["stream"])
+
+
+def test_append_rejects_bad_arguments_on_host(L):
+    assert _append(B=0) == _lib.MLA_OK
+    assert _append(B=0, kv=None) == _lib.MLA_OK            # empty batch: nothing to do
+    assert _append(kv=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append(kr=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append(pos=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append(table=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append(cache=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append(B=-1) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append(NB=0) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append(M=0) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append(kvs=504) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append(krs=56) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append(BS=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert _append(BS=8) == _lib.MLA_ERR_UNSUPPORTED
+    assert _append(BS=2048) == _lib.MLA_ERR_UNSUPPORTED
+    assert _append(M=1 << 24, BS=64) == _lib.MLA_ERR_UNSUPPORTED  # M*BS > 2^28
+    assert _append(kvs=580) == _lib.MLA_ERR_ALIGNMENT           # rows not 16-byte aligned
+    assert _append(krs=68) == _lib.MLA_ERR_ALIGNMENT
+    assert _append(kv=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    assert _append(kr=FAKE + 1030) == _lib.MLA_ERR_ALIGNMENT
+    assert _append(cache=FAKE + 4) == _lib.MLA_ERR_ALIGNMENT
+    assert _append(pos=FAKE + 2) == _lib.MLA_ERR_ALIGNMENT
+    assert _append(skipped=FAKE + 1) == _lib.MLA_ERR_ALIGNMENT
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
