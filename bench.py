@@ -173,6 +173,50 @@ def append_record(w, reps: int = 200) -> dict:
             "gb_s": moved / t / 1e9}
 
 
+def absorb_record(B: int, H: int, reps: int = 100) -> dict:
+    """Query absorption and value up-projection at the decode's batch shape,
+    with random weights of the layer's shape (W_UK, W_UV: [H, 128, 512] bf16).
+    HIP events around `reps` launches of each; bytes are the weights plus the
+    activations read and written once."""
+    import torch
+    import mla_latent_cache_absorbed_amd as mla
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(11)
+    q_in = torch.randn((B, H, 192), generator=g, device=dev).to(torch.bfloat16)
+    w_uk = (torch.randn((H, 128, 512), generator=g, device=dev) / 128 ** 0.5).to(torch.bfloat16)
+    w_uv = (torch.randn((H, 128, 512), generator=g, device=dev) / 512 ** 0.5).to(torch.bfloat16)
+    out = torch.randn((B, H, 512), generator=g, device=dev).to(torch.bfloat16)
+    w_uk_t = mla.absorb_prepare(w_uk)
+    q = torch.empty((B, H, 576), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    flops = 2.0 * B * H * 128 * 512
+    res = {}
+    for name, fn, nbytes in [
+            ("absorb_query", lambda: mla.absorb_query(q_in, w_uk_t, q),
+             H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 576 * 2),
+            ("up_project", lambda: mla.up_project(out, w_uv, o),
+             H * 128 * 512 * 2 + B * H * 512 * 2 + B * H * 128 * 2)]:
+        t = timed(fn)
+        gbs = nbytes / t / 1e9
+        res[name] = {"kernel": "mla_head_gemm_kernel", "launch_us": t * 1e6,
+                     "algorithmic_bytes": nbytes, "gb_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                     "tflops": flops / t / 1e12}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +341,7 @@ def main():
         "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
     }
     rec["append"] = append_record(w0)
+    rec["absorb"] = absorb_record(B, H)
     rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -19,7 +19,8 @@ import torch
 from . import _lib
 from ._lib import MlaError  # noqa: F401
 
-__all__ = ["decode", "Workspace", "plan", "attend", "append_latent", "MlaError"]
+__all__ = ["decode", "Workspace", "plan", "attend", "append_latent", "absorb_prepare",
+           "absorb_query", "up_project", "MlaError"]
 
 
 def _stream() -> int:
@@ -146,3 +147,48 @@ def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Ten
                                 skipped.data_ptr() if skipped is not None else None,
                                 B, NB, BS, M, _stream())
     _lib._check("mla_append_latent", st)
+
+
+def _bf16_contig(name, t, shape):
+    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def absorb_prepare(w_uk: torch.Tensor) -> torch.Tensor:
+    """W_UK [H, 128, 512] -> its per-head transpose [H, 512, 128], the layout
+    absorb_query reads (done once, when the weights are loaded)."""
+    H = w_uk.shape[0]
+    _bf16_contig("w_uk", w_uk, (H, 128, 512))
+    w_t = torch.empty((H, 512, 128), dtype=torch.bfloat16, device=w_uk.device)
+    _lib._check("mla_absorb_prepare", _lib.mla_absorb_prepare(w_uk.data_ptr(), w_t.data_ptr(), H, _stream()))
+    return w_t
+
+
+def absorb_query(q_in: torch.Tensor, w_uk_t: torch.Tensor, q: Optional[torch.Tensor] = None
+                 ) -> torch.Tensor:
+    """q_in [B, H, 192] (nope 128, then RoPE 64) -> absorbed query q [B, H, 576]."""
+    B, H = q_in.shape[0], q_in.shape[1]
+    _bf16_contig("q_in", q_in, (B, H, 192))
+    _bf16_contig("w_uk_t", w_uk_t, (H, 512, 128))
+    if q is None:
+        q = torch.empty((B, H, 576), dtype=torch.bfloat16, device=q_in.device)
+    _bf16_contig("q", q, (B, H, 576))
+    _lib._check("mla_absorb_query",
+                _lib.mla_absorb_query(q_in.data_ptr(), w_uk_t.data_ptr(), q.data_ptr(), B, H, _stream()))
+    return q
+
+
+def up_project(out: torch.Tensor, w_uv: torch.Tensor, o: Optional[torch.Tensor] = None
+               ) -> torch.Tensor:
+    """Decode output out [B, H, 512] -> value heads o [B, H, 128] = W_UV[h] out[b, h]."""
+    B, H = out.shape[0], out.shape[1]
+    _bf16_contig("out", out, (B, H, 512))
+    _bf16_contig("w_uv", w_uv, (H, 128, 512))
+    if o is None:
+        o = torch.empty((B, H, 128), dtype=torch.bfloat16, device=out.device)
+    _bf16_contig("o", o, (B, H, 128))
+    _lib._check("mla_up_project",
+                _lib.mla_up_project(out.data_ptr(), w_uv.data_ptr(), o.data_ptr(), B, H, _stream()))
+    return o

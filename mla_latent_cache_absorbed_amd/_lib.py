@@ -1,5 +1,5 @@
-"""ctypes binding of ``libmla_decode.so`` (C ABI in ``include/mla_decode.h`` and
-``include/mla_append.h``).
+"""ctypes binding of ``libmla_decode.so`` (C ABI in ``include/mla_decode.h``,
+``include/mla_append.h`` and ``include/mla_absorb.h``).
 
 Argument marshalling only: every step of the decode runs in the HIP library.
 The library must have been built (``python -m mla_latent_cache_absorbed_amd.build``
@@ -40,6 +40,9 @@ SIGNATURES = {
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_decode_abi_version": (_I, []),
     "mla_append_latent": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "mla_absorb_prepare": (_I, [_P, _P, _I, _P]),
+    "mla_absorb_query": (_I, [_P, _P, _P, _I, _I, _P]),
+    "mla_up_project": (_I, [_P, _P, _P, _I, _I, _P]),
 }
 
 _lib = None
@@ -115,3 +118,15 @@ def mla_append_latent(kv_c, kv_c_stride, k_rope, k_rope_stride, positions, block
                       latent_cache, skipped, B, NB, BS, M, stream) -> int:
     return lib().mla_append_latent(kv_c, kv_c_stride, k_rope, k_rope_stride, positions,
                                    block_table, latent_cache, skipped, B, NB, BS, M, stream)
+
+
+def mla_absorb_prepare(w_uk, w_uk_t, H, stream) -> int:
+    return lib().mla_absorb_prepare(w_uk, w_uk_t, H, stream)
+
+
+def mla_absorb_query(q_in, w_uk_t, q, B, H, stream) -> int:
+    return lib().mla_absorb_query(q_in, w_uk_t, q, B, H, stream)
+
+
+def mla_up_project(out, w_uv, o, B, H, stream) -> int:
+    return lib().mla_up_project(out, w_uv, o, B, H, stream)

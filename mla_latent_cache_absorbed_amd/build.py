@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "mla_decode.hip")
-SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_append.hip")]
+SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_append.hip"), os.path.join(HERE, "csrc", "mla_absorb.hip")]
 LIB = os.path.join(HERE, "libmla_decode.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -277,6 +277,51 @@ def absorb_query(q_nope: np.ndarray, q_rope: np.ndarray, W_UK: np.ndarray
 
 
 # ---------------------------------------------------------------------------
+# the products either side of the absorbed decode
+# ---------------------------------------------------------------------------
+
+D_NOPE = 128    # nope part of a query head
+D_VHEAD = 128   # value head width
+
+
+def oracle_absorb_query(q_in, W_UK) -> np.ndarray:
+    """Absorbed decode query of every request and head, float64 [B, H, 576].
+
+    q_in [B, H, 192]: per head the 128-wide nope part, then the 64-wide RoPE
+    part; W_UK [H, 128, 512]: head h's key up-projection (key = W_UK[h] kv_c).
+    The score of the explicit form, q_nope . (W_UK[h] kv_c) + q_rope . k_rope,
+    equals [W_UK[h]^T q_nope ; q_rope] . [kv_c ; k_rope] (page "DP attention +
+    expert parallel: MLA KV replication", section "A strong answer": the query
+    is moved into the latent space instead of the keys out of it).
+    """
+    qf = as_f64(q_in)
+    W = as_f64(W_UK)
+    B, H, _ = qf.shape
+    q = np.zeros((B, H, D_LATENT))
+    for h in range(H):
+        q[:, h, :D_KVC] = qf[:, h, :D_NOPE] @ W[h]      # [B,128] @ [128,512]
+        q[:, h, D_KVC:] = qf[:, h, D_NOPE:D_NOPE + D_ROPE]
+    return q
+
+
+def oracle_up_project(out, W_UV) -> np.ndarray:
+    """Value-head outputs, float64 [B, H, 128]: o[b,h] = W_UV[h] @ out[b,h].
+
+    out [B, H, 512] is the absorbed decode's latent-space output (attention
+    weights applied to kv_c); W_UV [H, 128, 512] is head h's value
+    up-projection (value = W_UV[h] kv_c), so W_UV[h] sum_t p_t kv_c_t is the
+    explicit form's sum_t p_t v_t.
+    """
+    of = as_f64(out)
+    W = as_f64(W_UV)
+    B, H, _ = of.shape
+    o = np.zeros((B, H, D_VHEAD))
+    for h in range(H):
+        o[:, h, :] = of[:, h, :] @ W[h].T               # [B,512] @ [512,128]
+    return o
+
+
+# ---------------------------------------------------------------------------
 # scalar brute force (tiny inputs only)
 # ---------------------------------------------------------------------------
 

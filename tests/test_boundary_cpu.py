@@ -160,6 +160,28 @@ def test_append_rejects_bad_arguments_on_host(L):
     assert _append(skipped=FAKE + 1) == _lib.MLA_ERR_ALIGNMENT
 
 
+def test_absorb_rejects_bad_arguments_on_host(L):
+    P, Q, U = _lib.mla_absorb_prepare, _lib.mla_absorb_query, _lib.mla_up_project
+    assert P(None, FAKE, 128, None) == _lib.MLA_ERR_NULL_POINTER
+    assert P(FAKE, None, 128, None) == _lib.MLA_ERR_NULL_POINTER
+    assert P(FAKE, FAKE, 0, None) == _lib.MLA_ERR_BAD_SHAPE
+    assert P(FAKE, FAKE, 129, None) == _lib.MLA_ERR_UNSUPPORTED
+    assert P(FAKE + 2, FAKE, 128, None) == _lib.MLA_ERR_ALIGNMENT
+    for F in (Q, U):
+        assert F(FAKE, FAKE, FAKE, 0, 128, None) == _lib.MLA_OK      # empty batch
+        assert F(None, FAKE, FAKE, 0, 128, None) == _lib.MLA_OK
+        assert F(None, FAKE, FAKE, 4, 128, None) == _lib.MLA_ERR_NULL_POINTER
+        assert F(FAKE, None, FAKE, 4, 128, None) == _lib.MLA_ERR_NULL_POINTER
+        assert F(FAKE, FAKE, None, 4, 128, None) == _lib.MLA_ERR_NULL_POINTER
+        assert F(FAKE, FAKE, FAKE, -1, 128, None) == _lib.MLA_ERR_BAD_SHAPE
+        assert F(FAKE, FAKE, FAKE, 4, 0, None) == _lib.MLA_ERR_BAD_SHAPE
+        assert F(FAKE, FAKE, FAKE, 4, 129, None) == _lib.MLA_ERR_UNSUPPORTED
+        assert F(FAKE, FAKE, FAKE, (1 << 24) + 1, 128, None) == _lib.MLA_ERR_UNSUPPORTED
+        assert F(FAKE + 8, FAKE, FAKE, 4, 128, None) == _lib.MLA_ERR_ALIGNMENT
+        assert F(FAKE, FAKE + 4, FAKE, 4, 128, None) == _lib.MLA_ERR_ALIGNMENT
+        assert F(FAKE, FAKE, FAKE + 2, 4, 128, None) == _lib.MLA_ERR_ALIGNMENT
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
