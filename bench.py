@@ -217,6 +217,63 @@ def absorb_record(B: int, H: int, reps: int = 100) -> dict:
     return res
 
 
+def fp8_record(w, layers_copies: int, steps: int, warmup: int) -> dict:
+    """The same decode step over an FP8 (e4m3) copy of the workload's cache:
+    fresh fp8 caches rotated like the bf16 ones, plan + attend per step, HIP
+    events around every attend launch."""
+    import torch
+    import mla_latent_cache_absorbed_amd as mla
+    from mla_latent_cache_absorbed_amd import accounting as acc
+    from mla_latent_cache_absorbed_amd import workloads as wl
+    dev = w.q.device
+    kv = wl.DEFAULT_KV_SCALE
+    caches = [wl.fp8_cache(w.cache, kv)]
+    for i in range(1, layers_copies):
+        g = torch.Generator(device=dev).manual_seed(2000 + i)
+        c = torch.randn(w.cache.shape, generator=g, device=dev).to(torch.bfloat16)
+        caches.append(wl.fp8_cache(c, kv))
+        del c
+    B, H, M, BS = w.B, w.H, w.M, w.BS
+    ws = mla.Workspace(B, H, M, BS, dev)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    def step(i, ev=None):
+        mla.plan(w.seq_lens, H, M, BS, ws)
+        if ev is not None:
+            ev[0].record()
+        mla.attend_fp8(w.q, caches[i % len(caches)], w.block_table, w.scale, kv, out, lse, ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(warmup + i, pairs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    att = sorted(a.elapsed_time(b) for a, b in pairs)
+    att_avg = sum(att) / len(att)
+    seq = w.seq_lens_list()
+    alg_bytes = acc.algorithmic_bytes(seq, H, BS, row_bytes=576)
+    alg_flops = acc.algorithmic_flops(seq, H)
+    gbs = alg_bytes / (att_avg * 1e-3) / 1e9
+    tfs = alg_flops / (att_avg * 1e-3) / 1e12
+    del caches
+    return {"kernel": "mla_attend_kernel<fp8>", "kv_scale": kv, "ms_per_step": ms_step,
+            "value": acc.token_reads(seq) / (ms_step * 1e-3), "unit": "cached-token reads/s",
+            "launch_ms": att_avg, "launch_ms_median": att[len(att) // 2], "launch_ms_min": att[0],
+            "algorithmic_bytes_per_launch": alg_bytes, "achieved_gb_s": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "mfma_tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -340,6 +397,8 @@ def main():
         },
         "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
     }
+    if H > 32 and BS >= 32 and name != "step61":
+        rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup)
     rec["append"] = append_record(w0)
     rec["absorb"] = absorb_record(B, H)
     rec["attainable"] = attainable_peaks(achieved_gbs, tflops)

@@ -135,6 +135,37 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* FP8 latent cache.  The cache holds one byte per element, OCP e4m3 (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F and
+ * 0xFF are NaN), 576 bytes per token: [NB, BS, 576], elements 0..511 kv_c
+ * and 512..575 k_rope as for bf16.  The pages price the cache at 576 bytes
+ * per token and layer in FP8 (page "MLA 的 TP 切分：为什么 8 张 GPU 存了同一份
+ * KV cache", sections 2.3 and 5.1) but give no scale convention; here one
+ * fp32 scale per cache dequantises every element: c_t[d] = kv_scale *
+ * e4m3(latent_cache[...][d]).  The result is the bf16 decode above over that
+ * dequantised cache:
+ *
+ *   s_t = scale * kv_scale * sum_d q[b,h,d] * e4m3(c8_t[d])
+ *   out = kv_scale * sum_t softmax_t(s) * e4m3(c8_t[0:512])
+ *
+ * (e4m3 values are exact in bf16, so products are exact and accumulate in
+ * fp32 as for a bf16 cache.)  Supported: 33 <= H <= 128 and BS >= 32
+ * (otherwise MLA_ERR_UNSUPPORTED); kv_scale finite (else MLA_ERR_BAD_SCALE).
+ * Everything else (plan, workspace, layouts of q, block_table, seq_lens,
+ * out, lse, errors) is as for mla_decode / mla_decode_attend; the plan call
+ * is shared. */
+mla_status mla_decode_fp8(const void* q, const void* latent_cache_fp8,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          float scale, float kv_scale, void* out, float* lse,
+                          int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache_fp8,
+                                 const int32_t* block_table, float scale, float kv_scale,
+                                 void* out, float* lse,
+                                 int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then copies the data-check word of the workspace
  * into *flags (0 = no violation seen since the last plan). */
 mla_status mla_decode_read_error(const void* workspace, int32_t* flags, void* stream);

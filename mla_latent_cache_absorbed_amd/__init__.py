@@ -19,8 +19,8 @@ import torch
 from . import _lib
 from ._lib import MlaError  # noqa: F401
 
-__all__ = ["decode", "Workspace", "plan", "attend", "append_latent", "absorb_prepare",
-           "absorb_query", "up_project", "MlaError"]
+__all__ = ["decode", "Workspace", "plan", "attend", "decode_fp8", "attend_fp8", "append_latent",
+           "absorb_prepare", "absorb_query", "up_project", "MlaError"]
 
 
 def _stream() -> int:
@@ -95,6 +95,56 @@ def decode(q: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tenso
                          B, H, NB, BS, M, ws.ptr, ws.nbytes, _stream())
     _lib._check("mla_decode", st)
     return out, lse
+
+
+def _check_fp8_inputs(q, cache8, table, lens):
+    if cache8.dtype != torch.uint8 or cache8.dim() != 3 or cache8.shape[2] != 576:
+        raise TypeError("latent_cache_fp8 must be a uint8 [NB, BS, 576] tensor of e4m3 bytes")
+    if not (q.is_cuda and cache8.is_cuda and table.is_cuda and lens.is_cuda):
+        raise ValueError("all inputs must be GPU tensors")
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 576:
+        raise ValueError("q must be bfloat16 [B, H, 576]")
+    if table.dtype != torch.int32 or lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    B = q.shape[0]
+    if table.dim() != 2 or table.shape[0] != B or lens.shape != (B,):
+        raise ValueError("block_table must be [B, M] and seq_lens [B]")
+    for t in (q, cache8, table, lens):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+
+
+def decode_fp8(q: torch.Tensor, latent_cache_fp8: torch.Tensor, block_table: torch.Tensor,
+               seq_lens: torch.Tensor, scale: float, kv_scale: float,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               workspace: Optional[Workspace] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Absorbed MLA decode over an FP8 (e4m3) latent cache whose values are
+    kv_scale * e4m3(byte); 33 <= H <= 128 and blocks of 32 tokens or more."""
+    _check_fp8_inputs(q, latent_cache_fp8, block_table, seq_lens)
+    B, H, _ = q.shape
+    NB, BS, _ = latent_cache_fp8.shape
+    M = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws = _ws(workspace, B, H, M, BS, q.device)
+    st = _lib.mla_decode_fp8(q.data_ptr(), latent_cache_fp8.data_ptr(), block_table.data_ptr(),
+                             seq_lens.data_ptr(), float(scale), float(kv_scale), out.data_ptr(),
+                             lse.data_ptr(), B, H, NB, BS, M, ws.ptr, ws.nbytes, _stream())
+    _lib._check("mla_decode_fp8", st)
+    return out, lse
+
+
+def attend_fp8(q, latent_cache_fp8, block_table, scale, kv_scale, out, lse,
+               workspace: Workspace) -> None:
+    B, H, _ = q.shape
+    NB, BS, _ = latent_cache_fp8.shape
+    M = block_table.shape[1]
+    st = _lib.mla_decode_attend_fp8(q.data_ptr(), latent_cache_fp8.data_ptr(), block_table.data_ptr(),
+                                    float(scale), float(kv_scale), out.data_ptr(), lse.data_ptr(),
+                                    B, H, NB, BS, M, workspace.ptr, workspace.nbytes, _stream())
+    _lib._check("mla_decode_attend_fp8", st)
 
 
 def plan(seq_lens: torch.Tensor, H: int, M: int, BS: int, workspace: Workspace,

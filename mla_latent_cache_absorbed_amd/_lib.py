@@ -40,6 +40,8 @@ SIGNATURES = {
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_decode_abi_version": (_I, []),
     "mla_append_latent": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "mla_decode_fp8": (_I, [_P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "mla_decode_attend_fp8": (_I, [_P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_absorb_prepare": (_I, [_P, _P, _I, _P]),
     "mla_absorb_query": (_I, [_P, _P, _P, _I, _I, _P]),
     "mla_up_project": (_I, [_P, _P, _P, _I, _I, _P]),
@@ -130,3 +132,15 @@ def mla_absorb_query(q_in, w_uk_t, q, B, H, stream) -> int:
 
 def mla_up_project(out, w_uv, o, B, H, stream) -> int:
     return lib().mla_up_project(out, w_uv, o, B, H, stream)
+
+
+def mla_decode_fp8(q, latent_cache, block_table, seq_lens, scale, kv_scale, out, lse,
+                   B, H, NB, BS, M, workspace, workspace_bytes, stream) -> int:
+    return lib().mla_decode_fp8(q, latent_cache, block_table, seq_lens, scale, kv_scale, out, lse,
+                                B, H, NB, BS, M, workspace, workspace_bytes, stream)
+
+
+def mla_decode_attend_fp8(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H, NB, BS,
+                          M, workspace, workspace_bytes, stream) -> int:
+    return lib().mla_decode_attend_fp8(q, latent_cache, block_table, scale, kv_scale, out, lse,
+                                       B, H, NB, BS, M, workspace, workspace_bytes, stream)

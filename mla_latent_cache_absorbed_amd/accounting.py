@@ -7,6 +7,8 @@ Bytes counted per call (one layer):
 * the queries (576 bf16 per head), the outputs (512 bf16 per head) and the
   fp32 log-sum-exp per head.
 
+With an FP8 cache a token's latent is 576 B (one byte per element).
+
 Flops: per (request, head, token), 2*576 for the score and 2*512 for the
 weighted sum of the ``kv_c`` part.  Split-KV partials are scratch traffic of
 a particular kernel design and are not part of the algorithmic figure.
@@ -25,9 +27,10 @@ def cache_bytes(seq_lens: Sequence[int]) -> int:
     return ROW_BYTES * sum(int(L) for L in seq_lens)
 
 
-def algorithmic_bytes(seq_lens: Sequence[int], H: int, BS: int) -> int:
+def algorithmic_bytes(seq_lens: Sequence[int], H: int, BS: int, row_bytes: int = ROW_BYTES) -> int:
+    """Bytes of one call; ``row_bytes`` = 576 for an FP8 cache."""
     B = len(seq_lens)
-    per_req = sum(ROW_BYTES * int(L) + 4 * (-(-int(L) // BS)) + 4 for L in seq_lens)
+    per_req = sum(row_bytes * int(L) + 4 * (-(-int(L) // BS)) + 4 for L in seq_lens)
     return per_req + B * H * (Q_BYTES + OUT_BYTES + LSE_BYTES)
 
 

@@ -196,6 +196,13 @@ __device__ __forceinline__ void qk_mfma_first(f32x16& acc, const bf16x8& a, cons
 __device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// the same with two wait states first, for operands just converted by the VALU
+__device__ __forceinline__ void qk_mfma_first_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void qk_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
@@ -226,7 +233,8 @@ struct AttendArgs {
   float* part_lse;       // [cap, Hp]  log2-domain log-sum-exp of each split item
   float* part_o;         // [cap, Hp * 512] normalised output of each split item, in the
                          // accumulator layout of the waves (see the epilogue)
-  float scale_log2;      // scale * log2(e)
+  float scale_log2;      // scale * log2(e) (times the fp8 cache scale for an fp8 cache)
+  float v_scale;         // fp8 cache scale applied to the output (1 for a bf16 cache)
   int32_t B, H, NB, M, lgBS;
 };
 
@@ -335,14 +343,15 @@ struct StageOne {
   uint32_t row0;             // byte offset of the stage's first row in the block
   uint32_t rowlast;          // byte offset of its last row before t1: later rows load that one
 };
+template <int kRowBytes = kD * 2>
 __device__ __forceinline__ StageOne stage_one(const AttendArgs& a, int b, int base, int t1, int& bad) {
   const CONST_AS int32_t* trow = (const CONST_AS int32_t*)(a.table) + size_t(b) * a.M;
   int blk = trow[base >> a.lgBS];
   if ((unsigned)blk >= (unsigned)a.NB) { blk = 0; bad = 1; }
   StageOne s;
-  s.r = block_rsrc(reinterpret_cast<const char*>(a.cache), blk, uint32_t(kD * 2) << a.lgBS);
-  s.row0 = uint32_t(base & ((1 << a.lgBS) - 1)) * (kD * 2);
-  s.rowlast = s.row0 + uint32_t(min(t1 - 1 - base, kSub - 1)) * (kD * 2);
+  s.r = block_rsrc(reinterpret_cast<const char*>(a.cache), blk, uint32_t(kRowBytes) << a.lgBS);
+  s.row0 = uint32_t(base & ((1 << a.lgBS) - 1)) * kRowBytes;
+  s.rowlast = s.row0 + uint32_t(min(t1 - 1 - base, kSub - 1)) * kRowBytes;
   return s;
 }
 // Row load with the swizzle given as a constant: lane_sw is this lane's 16
@@ -376,6 +385,78 @@ __device__ __forceinline__ void issue_one(const StageOne& s, char LDS_AS* sbuf, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 latent (OCP e4m3, one scale per cache).  A stage holds 32 rows of 576
+// bytes, row-major as in memory (with blocks of 32 tokens or more a stage is
+// one contiguous 18,432-byte run of its block, so its 18 loads of 1 KB are
+// fully coalesced), except that the 16-byte chunk c of token t sits at slot
+// c ^ x8(t) of its row: x8(t) = (t >> 2) & 3 keeps c within its aligned
+// group of four, and spreads the score reads (lanes 0..31 read 8 bytes of
+// one chunk of tokens 0..31; the row stride is 576 = 9 * 64 bytes) over
+// distinct bank groups.  Score operands are converted to bf16 in registers;
+// each wave converts its own column slab of kv_c to bf16 into the V slot, in
+// the bf16 stage's region-A layout, where the weighted sum reads it exactly
+// as for a bf16 cache.  e4m3 values are exact in bf16, so the products are
+// the same as for a bf16 cache holding the dequantised values divided by
+// the scale; the scale multiplies the scores and the output.
+// ---------------------------------------------------------------------------
+constexpr int kRow8 = kD;               // bytes per fp8 row
+constexpr int kStage8 = kSub * kRow8;   // 18,432 B
+constexpr int kLoads8 = kStage8 / 1024; // 18 loads of 1 KB per stage
+constexpr int kVSlot = kSub * 1024;     // bf16 kv_c of one stage
+
+__device__ __forceinline__ int x8(int t) { return (t >> 2) & 3; }
+
+// Load L (< 18) of a one-block fp8 stage: LDS bytes [1024 L, 1024 L + 1024).
+// Lane i's 16 bytes land at 1024 L + 16 i = row t, slot; they come from
+// chunk slot ^ x8(t) of row t (rows past t1 load the last valid row).
+__device__ __forceinline__ void issue_one8(const StageOne& s, char LDS_AS* sbuf, uint32_t lane16,
+                                           int L) {
+  const uint32_t o = uint32_t(L) * 1024 + lane16;
+  const uint32_t t = (o * 29128u) >> 24;  // o / 576, exact for o < 18,432
+  const uint32_t slot = (o - t * kRow8) >> 4;
+  const uint32_t chunk = slot ^ ((t >> 2) & 3);
+  dma16_plain(s.r, min(s.row0 + t * kRow8, s.rowlast) + chunk * 16, sbuf + L * 1024);
+}
+
+// 8 e4m3 values (low byte first) to bf16, exactly: one packed conversion per
+// pair of bytes (op_sel picks the high 16 bits of the source), with a unit
+// scale.  Written out: the compiler's lowering of the builtin for this
+// instruction was seen to return the first value of a pair for both.
+__device__ __forceinline__ uint32_t fp8x2_lo(uint32_t v) {
+  uint32_t r;
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(v));
+  return r;
+}
+__device__ __forceinline__ uint32_t fp8x2_hi(uint32_t v) {
+  uint32_t r;
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(v));
+  return r;
+}
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 v) {
+  return __builtin_bit_cast(bf16x8, i32x4{(int)fp8x2_lo(v[0]), (int)fp8x2_hi(v[0]),
+                                          (int)fp8x2_lo(v[1]), (int)fp8x2_hi(v[1])});
+}
+
+// Wave w's slab of kv_c (dims 512 w / NW .. +512 / NW) of an fp8 stage, to
+// bf16 in the V slot: lane l converts token l / 2, half l % 2 of the slab.
+template <int NW>
+__device__ __forceinline__ void convert_v8(const char LDS_AS* s8, char LDS_AS* vs, int w, int lane) {
+  constexpr int CH = 16 / NW;  // fp8 chunks per lane
+  const int t = lane >> 1;
+  const int c8 = (32 / NW) * w + CH * (lane & 1);
+  const int xt = x8(t), sa = swzA(t);
+  i32x4 raw[CH];
+#pragma unroll
+  for (int q = 0; q < CH; ++q) raw[q] = *(const i32x4 LDS_AS*)(s8 + t * kRow8 + 16 * (c8 + (q ^ xt)));
+#pragma unroll
+  for (int q = 0; q < CH; ++q) {
+    const int cb = 2 * (c8 + q);  // bf16 chunks cb, cb + 1
+    *(bf16x8 LDS_AS*)(vs + t * 1024 + 16 * (cb ^ sa)) = fp8x8_to_bf16(u32x2{(uint32_t)raw[q][0], (uint32_t)raw[q][1]});
+    *(bf16x8 LDS_AS*)(vs + t * 1024 + 16 * ((cb + 1) ^ sa)) = fp8x8_to_bf16(u32x2{(uint32_t)raw[q][2], (uint32_t)raw[q][3]});
+  }
+}
+
 template <bool V>
 struct BoolC {
   static constexpr bool value = V;
@@ -392,11 +473,17 @@ struct Pick<false, A, B> {
 constexpr int kWaveBytesM = 32 * kDV * 4;  // one wave's share of an item's partial
 
 // kOne: the block size is 32 tokens or more, so every stage lies in one block.
-template <int NW, int NS, bool kOne>
+// kF8: the cache is fp8 (e4m3); stages hold fp8 rows and one more LDS slot
+// holds the bf16 kv_c of the stage being summed.
+template <int NW, int NS, bool kOne, bool kF8 = false>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   static_assert(NW == 2 || NW == 4, "waves per workgroup");
   static_assert(NS >= 3, "the pipeline reads two stages while one more loads");
-  constexpr int LPW = kLoadsPerStage / NW;  // loads per wave per stage
+  static_assert(!kF8 || kOne, "fp8 stages are loaded from one block");
+  constexpr int kSB = kF8 ? kStage8 : kStageBytes;       // bytes of a ring stage
+  constexpr int kRing = NS * kSB + (kF8 ? kVSlot : 0);    // the ring (and the V slot)
+  // loads per wave per stage (fp8: 18 loads over NW waves, the last repeated)
+  constexpr int LPW = kF8 ? (kLoads8 + NW - 1) / NW : kLoadsPerStage / NW;
   constexpr int PFK = 4;                    // score operand reads in flight
   constexpr int PFV = 2;                    // weighted-sum operand reads in flight
   constexpr int HP = NW * 32;               // heads covered by the workgroup
@@ -405,9 +492,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   // LDS: the stage ring, then two buffers of weights.  Outside the stage loop
   // the first weight buffer holds instead the per-head row sums and
   // log-sum-exps being exchanged, the waves' redo votes and two scalars.
-  __shared__ __attribute__((aligned(1024))) char lds_raw[NS * kStageBytes + 2 * PBUF];
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kRing + 2 * PBUF];
   char LDS_AS* lds = (char LDS_AS*)(lds_raw);
-  char LDS_AS* const pw = lds + NS * kStageBytes;
+  char LDS_AS* const pw = lds + kRing;
+  char LDS_AS* const vslot = lds + NS * kSB;  // fp8 only
   float LDS_AS* const x_l = (float LDS_AS*)pw;          // [HP] row sums
   float LDS_AS* const x_lse = x_l + HP;                 // [HP] log2-domain log-sum-exps
   int LDS_AS* const s_vote = (int LDS_AS*)(x_lse + HP);  // [NW] redo votes
@@ -442,6 +530,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     for (int j = 0; j < 8; ++j) qk_off[j] = hl * 1024 + ((((2 * j) | hi)) ^ xa) * 16;
   }
   const int qkb = kRegionB + hi * 512 + hl * 16;
+  // fp8: k-step s reads 8 bytes of chunk s of token hl at qk8_off[s & 3] + 64 (s >> 2)
+  int qk8_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qk8_off[j] = hl * kRow8 + 16 * (j ^ x8(hl)) + 8 * hi;
   // Weighted sum.  Wave w owns columns 32 CPW w .. 32 CPW (w + 1) - 1 of O
   // for all HP heads: accumulator o[hb CPW + c] is O^T of the 32 columns of
   // block cb = CPW w + c for heads 32 hb .. 32 hb + 31.  So each wave reads
@@ -534,8 +626,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     bool first_pass = true;   // uniform: false on a redo
 
 #define MLA_KREAD(sb, s)                                                               \
-  ((s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))      \
-            : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
+  (kF8 ? fp8x8_to_bf16(*(const u32x2 LDS_AS*)((sb) + qk8_off[(s) & 3] + 64 * ((s) >> 2)))  \
+   : (s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))    \
+              : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
 #define MLA_VREAD(sb, f, dst)                                                               \
   do {                                                                                      \
     const int c_ = (f) % CPW, kk_ = (f) / CPW;                                              \
@@ -581,12 +674,22 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     auto stage_base = [&](int p) { return t0 + min(p, nst - 1) * kSub; };
     using Src = typename Pick<kOne, StageOne, StageIds>::T;
     auto src_of = [&](int base) -> Src {
-      if constexpr (kOne) return stage_one(a, b, base, t1, bad);
+      if constexpr (kF8) return stage_one<kRow8>(a, b, base, t1, bad);
+      else if constexpr (kOne) return stage_one(a, b, base, t1, bad);
       else return stage_ids(a, b, base, t1, bad);
     };
     auto issue = [&](const Src& sr, char LDS_AS* sbuf, int j) {
-      if constexpr (kOne) issue_one<NW>(sr, sbuf, w, lane_sw, rb_tok, rb_cp, j);
+      if constexpr (kF8) issue_one8(sr, sbuf, lane16, min(w + NW * j, kLoads8 - 1));
+      else if constexpr (kOne) issue_one<NW>(sr, sbuf, w, lane_sw, rb_tok, rb_cp, j);
       else issue_load<NW>(a, sr, sbuf, t1, w, lane16, j);
+    };
+    auto qk_first = [&](f32x16& acc, const bf16x8& x, const bf16x8& y) {
+      if constexpr (kF8) qk_mfma_first_v(acc, x, y);
+      else qk_mfma_first(acc, x, y);
+    };
+    auto qk_next = [&](f32x16& acc, const bf16x8& x, const bf16x8& y) {
+      if constexpr (kF8) qk_mfma_v(acc, x, y);
+      else qk_mfma(acc, x, y);
     };
     for (;;) {
       // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
@@ -615,7 +718,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       for (int p = 1; p < NS - 1; ++p) {
         const Src id = src_of(stage_base(p));
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) issue(id, lds + p * kStageBytes, j);
+        for (int j = 0; j < LPW; ++j) issue(id, lds + p * kSB, j);
       }
       Src nxt = src_of(stage_base(NS - 1));
       // stage 0 scores (a lone chain, once per item)
@@ -628,8 +731,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sb, s);
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
-          if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
-          else qk_mfma(sacc, kf[s % PFK], qreg[s]);
+          if (s == 0) qk_first(sacc, kf[0], qreg[0]);
+          else qk_next(sacc, kf[s % PFK], qreg[s]);
           if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sb, s + PFK);
         }
         qk_drain(sacc);
@@ -660,14 +763,20 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         }
         MLA_PWRITE(pw, 0, p0);
         MLA_PWRITE(pw, 1, p1);
+        if constexpr (kF8) {
+          convert_v8<NW>(lds, vslot, w, lane);
 #pragma unroll
-        for (int s = 0; s < PFV; ++s) MLA_VREAD(lds, s, vf[s]);
+          for (int s = 0; s < PFV; ++s) MLA_VREAD(vslot, s, vf[s]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < PFV; ++s) MLA_VREAD(lds, s, vf[s]);
+        }
       }
 
       auto iteration = [&](int k, auto mask_tag) {
         constexpr bool kMask = decltype(mask_tag)::value;
         constexpr int kDmaEvery = 36 / LPW;  // score MFMAs per load issued
-        const char LDS_AS* sbv = lds + (k % NS) * kStageBytes;
+        const char LDS_AS* sbv = kF8 ? vslot : lds + (k % NS) * kSB;
         const char LDS_AS* pcur = pw + (k & 1) * PBUF;
         char LDS_AS* pnxt = pw + ((k + 1) & 1) * PBUF;
         // stage k+1 and every wave's P(k) must be in LDS; stage k+2 may
@@ -675,9 +784,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         wait_vmcnt_lgkm0<LPW * (NS - 3)>();
         block_barrier();
         const Src cur = nxt;
-        char LDS_AS* sdst = lds + ((k + NS - 1) % NS) * kStageBytes;
+        char LDS_AS* sdst = lds + ((k + NS - 1) % NS) * kSB;
         nxt = src_of(stage_base(k + NS));
-        const char LDS_AS* sbk = lds + ((k + 1) % NS) * kStageBytes;
+        const char LDS_AS* sbk = lds + ((k + 1) % NS) * kSB;
         // With four waves each issues 9 loads per stage, spread between the
         // score MFMAs; a pair of waves issues its 18 in a burst (spread that
         // thin, every stall of the memory pipeline would land on an MFMA).
@@ -700,10 +809,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         // phase 1
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
-          if (s == 0) qk_mfma_first(sacc, kf[0], qreg[0]);
-          else qk_mfma(sacc, kf[s % PFK], qreg[s]);
+          if (s == 0) qk_first(sacc, kf[0], qreg[0]);
+          else qk_next(sacc, kf[s % PFK], qreg[s]);
           if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sbk, s + PFK);
-          if (kSpread && s % kDmaEvery == 0) issue(cur, sdst, s / kDmaEvery);
+          if (kSpread && s % kDmaEvery == 0 && s / kDmaEvery < LPW) issue(cur, sdst, s / kDmaEvery);
           if ((s & 1) && (s >> 1) < 16) pv_step(s >> 1);
         }
         qk_drain(sacc);
@@ -725,15 +834,24 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           if (v == 15) MLA_PWRITE(pnxt, 1, n1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // operands of the next weighted sum (stage k+1, already in LDS)
+        // operands of the next weighted sum (stage k+1, already in LDS; an
+        // fp8 stage's kv_c slab goes to the V slot first, after every read of
+        // stage k's)
+        if constexpr (kF8) {
+          asm volatile("" ::: "memory");
+          convert_v8<NW>(sbk, vslot, w, lane);
 #pragma unroll
-        for (int s = 0; s < PFV; ++s) MLA_VREAD(sbk, s, vf[s]);
+          for (int s = 0; s < PFV; ++s) MLA_VREAD(vslot, s, vf[s]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < PFV; ++s) MLA_VREAD(sbk, s, vf[s]);
+        }
       };
       for (int k = 0; k + 2 < nst; ++k) iteration(k, BoolC<false>{});
       if (nst >= 2) iteration(nst - 2, BoolC<true>{});
       {
         // weighted sum of the last stage, once every wave's weights are in
-        const char LDS_AS* sbv = lds + ((nst - 1) % NS) * kStageBytes;
+        const char LDS_AS* sbv = kF8 ? vslot : lds + ((nst - 1) % NS) * kSB;
         const char LDS_AS* pcur = pw + ((nst - 1) & 1) * PBUF;
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         block_barrier();
@@ -797,7 +915,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     __syncthreads();
     float inv[NW];
 #pragma unroll
-    for (int h = 0; h < NW; ++h) inv[h] = 1.0f / x_l[h * 32 + hl_e];
+    for (int h = 0; h < NW; ++h) {
+      if constexpr (kF8) inv[h] = a.v_scale / x_l[h * 32 + hl_e];
+      else inv[h] = 1.0f / x_l[h * 32 + hl_e];
+    }
     // out and lse of request b through buffer resources (32-bit lane
     // offsets); stores past the request's H heads fall outside the resource
     // and are dropped
@@ -916,8 +1037,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       // of up to 36: every load of a round is in flight at once, and the
       // blocks land in LDS in the layout they were stored in.  The
       // log-sum-exps load meanwhile.
-      char LDS_AS* mb = lds + w * kStageBytes;
-      constexpr int kRound = kStageBytes / 1024;  // 36 blocks
+      // (fp8: 32 KB per wave, within the ring and the V slot)
+      constexpr int kWaveBuf = kF8 ? 32 * 1024 : kStageBytes;
+      static_assert(NW * kWaveBuf <= kRing, "merge staging fits the ring");
+      char LDS_AS* mb = lds + w * kWaveBuf;
+      constexpr int kRound = kWaveBuf / 1024;  // 36 blocks (fp8: 32)
       constexpr int kBlocks = NW * CPW * 4;       // 64 blocks per wave
       auto blk_off = [&](int j) {  // block j = (h, c, g) of this wave's slab
         const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
@@ -1031,7 +1155,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     };
     // per-item log-sum-exps of this lane's head, then the weights, staged in
     // the LDS ring (free now) for up to kSlots items
-    constexpr int kSlots = NS * kStageBytes / (NW * 32 * 4);
+    constexpr int kSlots = kRing / (NW * 32 * 4);
     float LDS_AS* wsl = (float LDS_AS*)(lds) + w * 32 * kSlots + (lane_m & 31);
     const bool in_lds = cnt <= kSlots;
     // items' log-sum-exps in batches of 16, every load of a batch in flight
@@ -1890,6 +2014,47 @@ mla_status validate_attend(const void* q, const void* latent_cache, const int32_
   return check_workspace(workspace, workspace_bytes, B, H);
 }
 
+// The fp8 cache runs on the wide kernels (H > 32) with blocks of 32 tokens or more.
+mla_status validate_attend_fp8(const void* q, const void* latent_cache, const int32_t* block_table,
+                               float scale, float kv_scale, const void* out, const float* lse,
+                               int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                               const void* workspace, size_t workspace_bytes) {
+  mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
+                                 workspace, workspace_bytes);
+  if (s != MLA_OK) return s;
+  if (H <= 32 || BS < 32) return MLA_ERR_UNSUPPORTED;
+  if (!isfinite(kv_scale)) return MLA_ERR_BAD_SCALE;
+  return MLA_OK;
+}
+
+AttendArgs attend_args(const void* q, const void* latent_cache, const int32_t* block_table,
+                       float scale, float kv_scale, void* out, float* lse, int32_t B, int32_t H,
+                       int32_t NB, int32_t BS, int32_t M, void* workspace) {
+  const WsLayout L = ws_layout(B, H);
+  char* ws = static_cast<char*>(workspace);
+  AttendArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.cache = static_cast<const __bf16*>(latent_cache);
+  a.table = block_table;
+  a.out = static_cast<__bf16*>(out);
+  a.lse = lse;
+  a.hdr = reinterpret_cast<int32_t*>(ws);
+  a.req = reinterpret_cast<const int4*>(ws + L.req_off);
+  a.ctr = reinterpret_cast<int32_t*>(ws + L.ctr_off);
+  a.items = reinterpret_cast<const int4*>(ws + L.item_off);
+  a.big = reinterpret_cast<const int32_t*>(ws + L.big_off);
+  a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
+  a.part_o = reinterpret_cast<float*>(ws + L.po_off);
+  a.scale_log2 = scale * kv_scale * 1.4426950408889634f;
+  a.v_scale = kv_scale;
+  a.B = B;
+  a.H = H;
+  a.NB = NB;
+  a.M = M;
+  a.lgBS = ilog2_exact(BS);
+  return a;
+}
+
 mla_status validate_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t M, int32_t BS,
                          int32_t chunk_tokens, const void* workspace, size_t workspace_bytes) {
   mla_status s = check_sizes(B, H, M, BS);
@@ -1945,27 +2110,8 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
   if (s != MLA_OK || B == 0) return s;
   int ncu = 0;
   if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
-  const WsLayout L = ws_layout(B, H);
-  char* ws = static_cast<char*>(workspace);
-  AttendArgs a;
-  a.q = static_cast<const __bf16*>(q);
-  a.cache = static_cast<const __bf16*>(latent_cache);
-  a.table = block_table;
-  a.out = static_cast<__bf16*>(out);
-  a.lse = lse;
-  a.hdr = reinterpret_cast<int32_t*>(ws);
-  a.req = reinterpret_cast<const int4*>(ws + L.req_off);
-  a.ctr = reinterpret_cast<int32_t*>(ws + L.ctr_off);
-  a.items = reinterpret_cast<const int4*>(ws + L.item_off);
-  a.big = reinterpret_cast<const int32_t*>(ws + L.big_off);
-  a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
-  a.part_o = reinterpret_cast<float*>(ws + L.po_off);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.B = B;
-  a.H = H;
-  a.NB = NB;
-  a.M = M;
-  a.lgBS = ilog2_exact(BS);
+  const AttendArgs a = attend_args(q, latent_cache, block_table, scale, 1.0f, out, lse, B, H, NB,
+                                   BS, M, workspace);
   const Variant v = pick_variant(H);
   const int grid = ncu;  // one workgroup per compute unit
   hipStream_t st = (hipStream_t)stream;
@@ -1997,6 +2143,42 @@ mla_status mla_decode(const void* q, const void* latent_cache, const int32_t* bl
     return s;
   return mla_decode_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
                            workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache,
+                                 const int32_t* block_table, float scale, float kv_scale,
+                                 void* out, float* lse, int32_t B, int32_t H, int32_t NB,
+                                 int32_t BS, int32_t M, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  mla_status s = validate_attend_fp8(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H,
+                                     NB, BS, M, workspace, workspace_bytes);
+  if (s != MLA_OK || B == 0) return s;
+  int ncu = 0;
+  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  const AttendArgs a = attend_args(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H,
+                                   NB, BS, M, workspace);
+  hipStream_t st = (hipStream_t)stream;
+  // six fp8 stages (two loading ahead of the four in flight) fill the LDS
+  // with the V slot and the weight buffers
+  if (pick_variant(H).nw == 4)
+    hipLaunchKernelGGL((mla_attend_kernel<4, 6, true, true>), dim3(ncu), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((mla_attend_kernel<2, 6, true, true>), dim3(ncu), dim3(128), 0, st, a);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_fp8(const void* q, const void* latent_cache, const int32_t* block_table,
+                          const int32_t* seq_lens, float scale, float kv_scale, void* out,
+                          float* lse, int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status s = validate_attend_fp8(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H,
+                                     NB, BS, M, workspace, workspace_bytes);
+  if (s != MLA_OK || B == 0) return s;
+  if ((s = validate_plan(seq_lens, B, H, M, BS, 0, workspace, workspace_bytes)) != MLA_OK) return s;
+  if ((s = mla_decode_plan(seq_lens, B, H, M, BS, 0, workspace, workspace_bytes, stream)) != MLA_OK)
+    return s;
+  return mla_decode_attend_fp8(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H, NB,
+                               BS, M, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode_read_error(const void* workspace, int32_t* flags, void* stream) {

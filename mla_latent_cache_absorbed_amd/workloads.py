@@ -209,6 +209,20 @@ def make_custom(seq_lens: Sequence[int], H: int = 128, BS: int = 64,
                     lens.to(dev), scale)
 
 
+#: default fp8 cache scale: N(0, 1) latents divided by it stay well inside
+#: e4m3's range (largest finite 448) while small values keep their 3-bit
+#: mantissa (smallest normal 2^-6 * 0.0625)
+DEFAULT_KV_SCALE = 0.0625
+
+
+def fp8_cache(cache: torch.Tensor, kv_scale: float = DEFAULT_KV_SCALE) -> torch.Tensor:
+    """An fp8 cache from a bf16 one: each value divided by ``kv_scale`` and
+    rounded to OCP e4m3 by torch's conversion, returned as its uint8 bytes
+    (same shape, same device).  NaN stays NaN."""
+    x = (cache.float() / kv_scale).to(torch.float8_e4m3fn)
+    return x.view(torch.uint8)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Host copy of a bf16 tensor as uint16 bit patterns (what the oracle reads)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)

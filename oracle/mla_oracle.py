@@ -198,6 +198,52 @@ def merge_partials(parts: Sequence[Tuple[np.ndarray, np.ndarray]]
 
 
 # ---------------------------------------------------------------------------
+# FP8 latent cache
+# ---------------------------------------------------------------------------
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decode OCP FP8 E4M3 bytes: sign bit, 4 exponent bits (bias 7), 3
+    mantissa bits; exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN and
+    there are no infinities (so S.1111.110 = 448 is the largest finite)."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (b & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def oracle_decode_fp8(q, cache_fp8, block_table, seq_lens, scale, kv_scale,
+                      requests: Iterable[int] | None = None
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode over an FP8 latent cache [NB, BS, 576] of e4m3 bytes.
+
+    The pages give the cache as 576 bytes per token and layer in FP8 (page
+    "MLA 的 TP 切分…", sections 2.3 and 5.1) and no scale convention; the
+    reading taken is one scale per cache, element value = kv_scale *
+    e4m3(byte).  The attention is then the bf16 definition over those values
+    (:func:`attend_one`), gathered per request so that only its rows are
+    decoded.
+    """
+    qf = as_f64(q)
+    bt = np.asarray(block_table)
+    sl = np.asarray(seq_lens)
+    BS = cache_fp8.shape[1]
+    idx = list(range(qf.shape[0])) if requests is None else list(requests)
+    outs, lses = [], []
+    for b in idx:
+        L = int(sl[b])
+        t = np.arange(L)
+        rows = float(kv_scale) * e4m3_to_f64(np.asarray(cache_fp8)[np.asarray(bt[b])[t // BS], t % BS])
+        rows = rows.reshape(L, D_LATENT)
+        o, l = attend_one(qf[b], rows, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------------
 # paged append: the step that puts a new token into the cache
 # ---------------------------------------------------------------------------
 

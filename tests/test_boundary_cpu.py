@@ -160,6 +160,35 @@ def test_append_rejects_bad_arguments_on_host(L):
     assert _append(skipped=FAKE + 1) == _lib.MLA_ERR_ALIGNMENT
 
 
+def _decode8(**kw):
+    a = dict(q=FAKE, cache=FAKE, table=FAKE, lens=FAKE, scale=0.07, kv=0.0625, out=FAKE, lse=FAKE,
+             B=2, H=128, NB=14, BS=64, M=7, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return _lib.mla_decode_fp8(a["q"], a["cache"], a["table"], a["lens"], a["scale"], a["kv"],
+                               a["out"], a["lse"], a["B"], a["H"], a["NB"], a["BS"], a["M"],
+                               a["ws"], a["wsb"], a["stream"])
+
+
+def test_fp8_decode_rejects_bad_arguments_on_host(L):
+    assert _decode8(B=0) == _lib.MLA_OK
+    assert _decode8(H=32) == _lib.MLA_ERR_UNSUPPORTED     # the narrow kernel has no fp8 form
+    assert _decode8(H=1) == _lib.MLA_ERR_UNSUPPORTED
+    assert _decode8(BS=16) == _lib.MLA_ERR_UNSUPPORTED    # fp8 stages load from one block
+    assert _decode8(H=33, BS=32) != _lib.MLA_ERR_UNSUPPORTED
+    assert _decode8(kv=float("nan")) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode8(kv=float("inf")) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode8(scale=float("nan")) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode8(cache=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode8(lens=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _decode8(cache=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    assert _decode8(wsb=16) == _lib.MLA_ERR_WORKSPACE
+    A = _lib.mla_decode_attend_fp8
+    assert A(FAKE, FAKE, FAKE, 0.1, 0.5, FAKE, FAKE, 2, 16, 14, 64, 7, FAKE, 1 << 40, None) \
+        == _lib.MLA_ERR_UNSUPPORTED
+    assert A(FAKE, FAKE, FAKE, 0.1, float("nan"), FAKE, FAKE, 2, 128, 14, 64, 7, FAKE, 1 << 40,
+             None) == _lib.MLA_ERR_BAD_SCALE
+
+
 def test_absorb_rejects_bad_arguments_on_host(L):
     P, Q, U = _lib.mla_absorb_prepare, _lib.mla_absorb_query, _lib.mla_up_project
     assert P(None, FAKE, 128, None) == _lib.MLA_ERR_NULL_POINTER

@@ -1,0 +1,127 @@
+"""GPU parity of the FP8-cache decode (C ABI mla_decode_fp8 / mla_decode_attend_fp8)
+against the oracle, with the decode's gate: |out - ref| <= 1e-2 + 1e-2 |ref|,
+|lse - ref| <= 1e-3, non-finite output where the reference is finite fails.
+The caches are torch's e4m3 rounding of N(0, 1) latents over kv_scale; the
+oracle decodes the same bytes."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_cache_absorbed_amd import workloads as wl
+from oracle import mla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import mla_latent_cache_absorbed_amd as mla  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def _run(w, c8, kv, chunk=None, ws=None):
+    out = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=DEV)
+    if chunk is None:
+        mla.decode_fp8(w.q, c8, w.block_table, w.seq_lens, w.scale, kv, out, lse, workspace=ws)
+    else:
+        ws = ws or mla.Workspace(w.B, w.H, w.M, w.BS, DEV)
+        mla.plan(w.seq_lens, w.H, w.M, w.BS, ws, chunk_tokens=chunk)
+        mla.attend_fp8(w.q, c8, w.block_table, w.scale, kv, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(w, c8, kv, what, chunk=None, requests=None, ws=None):
+    out, lse = _run(w, c8, kv, chunk, ws)
+    ro, rl = orc.oracle_decode_fp8(wl.bf16_bits(w.q), c8.cpu().numpy(), w.block_table.cpu().numpy(),
+                                   w.seq_lens.cpu().numpy(), w.scale, kv, requests=requests)
+    if requests is not None:
+        out, lse = out[requests], lse[requests]
+    r = orc.parity_report(out, lse, ro, rl)
+    _say(f"[fp8] {what}: {r}")
+    assert r["ok"], f"{what}: {r}"
+
+
+def _gpu(w):
+    return wl.Workload(w.name, w.q.to(DEV), w.cache.to(DEV), w.block_table.to(DEV),
+                       w.seq_lens.to(DEV), w.scale)
+
+
+@pytest.mark.parametrize("H", [128, 100, 64, 48, 33])
+def test_fp8_heads(H):
+    w = _gpu(wl.make_custom([1, 31, 32, 33, 200, 0, 700], H=H, BS=64, seed=H, poison_unused=True))
+    _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"H={H}")
+
+
+@pytest.mark.parametrize("BS", [32, 64, 128, 256])
+def test_fp8_block_sizes(BS):
+    w = _gpu(wl.make_custom([5, 95, 300, 1000], H=128, BS=BS, seed=BS, poison_unused=True))
+    _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"BS={BS}")
+
+
+@pytest.mark.parametrize("kv", [1.0, 0.037, 3.5])
+def test_fp8_scales(kv):
+    w = _gpu(wl.make_custom([64, 130, 513], H=128, BS=64, seed=3))
+    _check(w, wl.fp8_cache(w.cache, kv), kv, f"kv_scale={kv}")
+
+
+@pytest.mark.parametrize("H,chunk", [(128, 32), (128, 96), (128, 1024), (48, 64), (48, 1024)])
+def test_fp8_forced_splits(H, chunk):
+    """Splits of two and of three or more items: partials carry the scale."""
+    w = _gpu(wl.make_custom([2000, 45, 700, 1], H=H, BS=32, seed=chunk, poison_unused=True))
+    _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"H={H} chunk={chunk}", chunk=chunk)
+
+
+def test_fp8_large_score_range_redo_path():
+    """A key far larger than the rest late in a request forces the redo path."""
+    w = wl.make_custom([600, 64], H=128, BS=64, seed=8)
+    q = w.q.float()
+    c = w.cache.float()
+    blk = int(w.block_table[0, 500 // 64])
+    c[blk, 500 % 64] = 0.0
+    c[blk, 500 % 64, :512] = torch.sign(q[0, 0, :512]) * 25.0  # 400 in e4m3 units at 1/16
+    w = _gpu(wl.Workload(w.name, w.q, c.to(torch.bfloat16), w.block_table, w.seq_lens, w.scale))
+    _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, "redo path")
+
+
+def test_fp8_full_size_dp_rank_sampled():
+    """The DP-rank shape (124 x 4,096, 128 heads, 64-token blocks) with an fp8
+    cache, in the launch configuration the benchmark times; sampled requests."""
+    w = wl.make("dp_rank", device=DEV, seed=0)
+    c8 = wl.fp8_cache(w.cache)
+    reqs = [0, 1, 61, 122, 123]
+    _check(w, c8, wl.DEFAULT_KV_SCALE, "dp_rank sampled", requests=reqs)
+
+
+def test_fp8_ragged_full_size_sampled():
+    w = wl.make("ragged", device=DEV, seed=0)
+    c8 = wl.fp8_cache(w.cache)
+    lens = w.seq_lens.cpu().numpy()
+    reqs = [int(np.argmax(lens)), int(np.argmin(lens)), 7]
+    _check(w, c8, wl.DEFAULT_KV_SCALE, "ragged sampled", requests=reqs)
+
+
+def test_fp8_matches_bf16_decode_of_dequantised_cache():
+    """The fp8 path equals the bf16 path over the dequantised cache (e4m3
+    values are exact in bf16; a power-of-two kv_scale keeps them exact)."""
+    w = _gpu(wl.make_custom([77, 1000, 3], H=128, BS=64, seed=12))
+    c8 = wl.fp8_cache(w.cache, 0.0625)
+    deq = (c8.view(torch.float8_e4m3fn).float() * 0.0625).to(torch.bfloat16)
+    o8, l8 = _run(w, c8, 0.0625)
+    wb = wl.Workload(w.name, w.q, deq, w.block_table, w.seq_lens, w.scale)
+    ob = torch.empty_like(torch.from_numpy(o8)).to(DEV).to(torch.bfloat16)
+    lb = torch.empty((w.B, w.H), dtype=torch.float32, device=DEV)
+    mla.decode(wb.q, wb.cache, wb.block_table, wb.seq_lens, wb.scale, ob, lb)
+    torch.cuda.synchronize()
+    # the same products and sums in the same order; the power-of-two scale
+    # only moves between the operands and the final factors, exactly
+    assert np.array_equal(o8, ob.float().cpu().numpy())
+    assert np.array_equal(l8, lb.cpu().numpy())
