@@ -484,7 +484,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   constexpr int kRing = NS * kSB + (kF8 ? kVSlot : 0);    // the ring (and the V slot)
   // loads per wave per stage (fp8: 18 loads over NW waves, the last repeated)
   constexpr int LPW = kF8 ? (kLoads8 + NW - 1) / NW : kLoadsPerStage / NW;
-  constexpr int PFK = 4;                    // score operand reads in flight
+  // score operand reads in flight (fp8: raw 8-byte fragments, each
+  // converted just before its MFMA)
+  constexpr int PFK = 4;
   constexpr int PFV = 2;                    // weighted-sum operand reads in flight
   constexpr int HP = NW * 32;               // heads covered by the workgroup
   constexpr int CPW = 16 / NW;              // 32-column blocks of O per wave
@@ -625,10 +627,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     float la = 0.0f, lb = 0.0f;  // this lane's share of the row sum, in two chains
     bool first_pass = true;   // uniform: false on a redo
 
-#define MLA_KREAD(sb, s)                                                               \
-  (kF8 ? fp8x8_to_bf16(*(const u32x2 LDS_AS*)((sb) + qk8_off[(s) & 3] + 64 * ((s) >> 2)))  \
-   : (s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))    \
-              : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
+    using KRaw = typename Pick<kF8, u32x2, bf16x8>::T;
+    auto kread = [&](const char LDS_AS* sb, int s) -> KRaw {
+      if constexpr (kF8) return *(const u32x2 LDS_AS*)(sb + qk8_off[s & 3] + 64 * (s >> 2));
+      else
+        return s < 32 ? *(const bf16x8 LDS_AS*)(sb + qk_off[s & 7] + 256 * (s >> 3))
+                      : *(const bf16x8 LDS_AS*)(sb + qkb + 1024 * (s - 32));
+    };
+    auto kcvt = [&](const KRaw& x) -> bf16x8 {
+      if constexpr (kF8) return fp8x8_to_bf16(x);
+      else return x;
+    };
 #define MLA_VREAD(sb, f, dst)                                                               \
   do {                                                                                      \
     const int c_ = (f) % CPW, kk_ = (f) / CPW;                                              \
@@ -726,14 +735,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       f32x16 sacc;
       {
         const char LDS_AS* sb = lds;
-        bf16x8 kf[PFK];
+        KRaw kf[PFK];
 #pragma unroll
-        for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sb, s);
+        for (int s = 0; s < PFK; ++s) kf[s] = kread(sb, s);
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
-          if (s == 0) qk_first(sacc, kf[0], qreg[0]);
-          else qk_next(sacc, kf[s % PFK], qreg[s]);
-          if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sb, s + PFK);
+          if constexpr (kF8) {
+            const bf16x8 kb = kcvt(kf[s % PFK]);
+            if (s + PFK < 36) kf[s % PFK] = kread(sb, s + PFK);
+            if (s == 0) qk_first(sacc, kb, qreg[0]);
+            else qk_next(sacc, kb, qreg[s]);
+          } else {
+            if (s == 0) qk_first(sacc, kf[0], qreg[0]);
+            else qk_next(sacc, kf[s % PFK], qreg[s]);
+            if (s + PFK < 36) kf[s % PFK] = kread(sb, s + PFK);
+          }
         }
         qk_drain(sacc);
       }
@@ -794,9 +810,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         if (!kSpread)
 #pragma unroll
           for (int j = 0; j < LPW; ++j) issue(cur, sdst, j);
-        bf16x8 kf[PFK];
+        KRaw kf[PFK];
 #pragma unroll
-        for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(sbk, s);
+        for (int s = 0; s < PFK; ++s) kf[s] = kread(sbk, s);
         bf16x8 pa[NW], pb[NW];  // P(k) fragments of the two token halves
 #pragma unroll
         for (int h = 0; h < NW; ++h) pa[h] = MLA_PREAD(pcur, h, 0);
@@ -809,9 +825,16 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         // phase 1
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
-          if (s == 0) qk_first(sacc, kf[0], qreg[0]);
-          else qk_next(sacc, kf[s % PFK], qreg[s]);
-          if (s + PFK < 36) kf[s % PFK] = MLA_KREAD(sbk, s + PFK);
+          if constexpr (kF8) {
+            const bf16x8 kb = kcvt(kf[s % PFK]);
+            if (s + PFK < 36) kf[s % PFK] = kread(sbk, s + PFK);
+            if (s == 0) qk_first(sacc, kb, qreg[0]);
+            else qk_next(sacc, kb, qreg[s]);
+          } else {
+            if (s == 0) qk_first(sacc, kf[0], qreg[0]);
+            else qk_next(sacc, kf[s % PFK], qreg[s]);
+            if (s + PFK < 36) kf[s % PFK] = kread(sbk, s + PFK);
+          }
           if (kSpread && s % kDmaEvery == 0 && s / kDmaEvery < LPW) issue(cur, sdst, s / kDmaEvery);
           if ((s & 1) && (s >> 1) < 16) pv_step(s >> 1);
         }
@@ -890,7 +913,6 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb) o[cb] = f32x16{};
     }
-#undef MLA_KREAD
 #undef MLA_VREAD
 #undef MLA_PREAD
 #undef MLA_PWRITE
