@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the fp8, append, absorption and attainable-peak records")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -397,11 +399,12 @@ def main():
         },
         "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
     }
-    if H > 32 and BS >= 32 and name != "step61":
-        rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup)
-    rec["append"] = append_record(w0)
-    rec["absorb"] = absorb_record(B, H)
-    rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
+    if not args.no_extras:
+        if H > 32 and BS >= 32 and name != "step61":
+            rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup)
+        rec["append"] = append_record(w0)
+        rec["absorb"] = absorb_record(B, H)
+        rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
