@@ -73,6 +73,11 @@ typedef enum {
 /* Bits of the data-check word raised in the workspace (see mla_decode_read_error). */
 #define MLA_CHECK_SEQ_LEN_RANGE 1  /* some seq_lens[b] < 0 or > M*BS (clamped)       */
 #define MLA_CHECK_BLOCK_ID_RANGE 2 /* some used block id outside [0, NB) (set to 0)  */
+#define MLA_CHECK_SCORE_RANGE 8    /* some request's scaled scores lie beyond what the
+                                      fp32 softmax resolves (about 2^30 in log2 units,
+                                      where one ulp exceeds the kernel's exponent
+                                      headroom of 64); that request's outputs are
+                                      unspecified                                     */
 #define MLA_CHECK_MERGE_WAIT 4     /* a split merge stopped waiting for its partners
                                       (never expected; outputs of that request are
                                       unspecified)                                    */

@@ -25,6 +25,8 @@ MLA_ERR_ALIGNMENT = 7
 
 MLA_CHECK_SEQ_LEN_RANGE = 1
 MLA_CHECK_BLOCK_ID_RANGE = 2
+MLA_CHECK_MERGE_WAIT = 4
+MLA_CHECK_SCORE_RANGE = 8
 
 #: every symbol the header declares, with (restype, argtypes)
 _P = ctypes.c_void_p

@@ -902,6 +902,16 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int h = 0; h < NW; ++h) redo |= s_vote[h];
       if (!__builtin_amdgcn_readfirstlane(redo)) break;
+      // One redo at most.  Its reference is each head's largest score of the
+      // item, so an excess left after it is fp32 rounding of scores beyond
+      // what the softmax resolves (scaled scores past about 2^30 in log2
+      // units, where one ulp exceeds the headroom).  Redoing again would
+      // not change the reference, so the request is flagged instead (its
+      // outputs are unspecified) and the item ends.
+      if (!first_pass) {
+        if (w == 0) lane0_atomic_or(&a.hdr[2], MLA_CHECK_SCORE_RANGE);
+        break;
+      }
       // Redo the item from its first stage with the head's largest score as
       // the reference.
       m_run += pair_max(amax);
@@ -1476,6 +1486,11 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
         }
       }
       if (__ballot(amax > kRefHeadroom) == 0) break;
+      // one redo at most, as in the wide kernel
+      if (!first_pass) {
+        lane0_atomic_or(&a.hdr[2], MLA_CHECK_SCORE_RANGE);
+        break;
+      }
       m_run += pair_max(amax);
       first_pass = false;
       amax = -INFINITY;

@@ -125,3 +125,14 @@ def test_fp8_matches_bf16_decode_of_dequantised_cache():
     # only moves between the operands and the final factors, exactly
     assert np.array_equal(o8, ob.float().cpu().numpy())
     assert np.array_equal(l8, lb.cpu().numpy())
+
+
+def test_fp8_scores_beyond_fp32_softmax_range_terminate():
+    """A cache scale of 2^40 puts the scaled scores far beyond what the fp32
+    softmax resolves: the call returns and raises at most the score-range bit."""
+    w = _gpu(wl.make_custom([300, 100], H=128, BS=32, seed=2))
+    ws = mla.Workspace(w.B, w.H, w.M, w.BS, DEV)
+    _run(w, wl.fp8_cache(w.cache), 2.0 ** 40, ws=ws)
+    flags = ws.check_flags()
+    _say(f"[fp8] huge scale: flags {flags}")
+    assert flags & ~mla._lib.MLA_CHECK_SCORE_RANGE == 0

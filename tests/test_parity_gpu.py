@@ -245,6 +245,29 @@ def test_large_score_range_redo_path():
     _assert_parity(out, lse, ro, rl, "redo path")
 
 
+@pytest.mark.parametrize("H", [128, 48, 16])
+def test_scores_beyond_fp32_softmax_range_terminate(H):
+    """Scaled scores near 2^41 (log2 units), where one fp32 ulp exceeds the
+    exponent headroom: the item is redone at most once, the call returns, at
+    most the score-range bit is raised, and a normal request in the same
+    batch is unaffected (regression: an unbounded redo never ended here)."""
+    lens = [300, 100]
+    w = wl.make_custom(lens, H=H, BS=32, seed=H, shuffle=False)
+    q = w.q.clone()
+    c = w.cache.clone()
+    q[0] = (q[0].float() * 2.0 ** 20).to(torch.bfloat16)
+    nb0 = -(-lens[0] // 32)
+    c[:nb0] = (c[:nb0].float() * 2.0 ** 20).to(torch.bfloat16)
+    w = _to_gpu(wl.Workload("huge", q, c, w.block_table, w.seq_lens, w.scale))
+    ws = mla.Workspace(w.B, w.H, w.M, w.BS, w.q.device)
+    out, lse = _run(w, ws=ws)
+    flags = ws.check_flags()
+    _say(f"[huge scores] H={H}: flags {flags}")
+    assert flags & ~mla._lib.MLA_CHECK_SCORE_RANGE == 0
+    ro, rl = _oracle(w, requests=[1])
+    _assert_parity(out[1:], lse[1:], ro, rl, f"normal request beside huge scores H={H}")
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads on sampled requests
 # ---------------------------------------------------------------------------
