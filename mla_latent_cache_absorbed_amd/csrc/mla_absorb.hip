@@ -40,6 +40,7 @@ constexpr int kDVH = 128;   // value head
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const __bf16* W;  // [H, N, K]
@@ -54,34 +55,40 @@ struct GemmArgs {
   int r_head;
 };
 
-// Workgroup i -> (head, group of NT n-tiles), with all groups of a head on
-// XCD i % 8.  Each wave computes NT 32x32 tiles of Y^T for one tile of 32
-// requests, so its X fragments serve NT products.  Loads are issued a batch
-// of kBatch k-steps ahead of the MFMAs that use them (scheduling barriers
-// keep the compiler from interleaving them one step at a time, which leaves
-// a wave waiting on each load in turn).  Measured at 124 requests x 128
-// heads: NT = 4, kBatch = 4 for the absorption (K = 128) and NT = 2,
-// kBatch = 4 for the up-projection (K = 512) were the fastest of the
-// shapes tried.
-template <int K, int NT, int kBatch>
-__global__ __launch_bounds__(256) void mla_head_gemm_kernel(GemmArgs a) {
-  constexpr int kSteps = K / 16;
-  constexpr int kBatches = kSteps / kBatch;
-  static_assert(kSteps % kBatch == 0, "K / 16 must be a multiple of the batch");
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int T = a.N / (32 * NT);
+// Workgroup (i, y) -> head h and group ng of NT n-tiles (all groups of a
+// head on XCD i % 8, so its X rows come from HBM once and then from that
+// XCD's L2), requests 128 y .. 128 y + 127.  K goes in chunks of 128: the
+// workgroup stages the chunk of its 32 NT rows of W and of its 128 X rows in
+// LDS with coalesced 16-byte loads (each row's 256 bytes are contiguous),
+// then each wave multiplies its 32 requests by the NT n-tiles from LDS.  The
+// 16-byte chunk c of LDS row r sits at slot c ^ (r % 16), so the fragment
+// reads of 32 rows at one chunk hit distinct banks.
+constexpr int kKC = 128;                 // K per LDS chunk
+constexpr int kRowB = kKC * 2;           // bytes per LDS row
+
+__device__ __forceinline__ int lds_slot(int row, int c16) { return row * kRowB + 16 * (c16 ^ (row & 15)); }
+
+template <int K, int NT>
+__global__ __launch_bounds__(256, 2) void mla_head_gemm_kernel(GemmArgs a) {
+  static_assert(K % kKC == 0, "K is a multiple of the chunk");
+  constexpr int kWRows = 32 * NT;
+  constexpr int kXRows = 128;
+  constexpr int kLoads = (kWRows + kXRows) * (kRowB / 16) / 256;  // 16-byte loads per thread
+  __shared__ __attribute__((aligned(16))) char lds[(kWRows + kXRows) * kRowB];
+  char* const lw = lds;
+  char* const lx = lds + kWRows * kRowB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int T = a.N / kWRows;
   const int i = blockIdx.x;
   const int r = i >> 3;
   const int h = (i & 7) + 8 * (r / T);
   const int ng = r % T;
-  const int b0 = 128 * blockIdx.y + 32 * w;
-  if (h >= a.H || b0 >= a.B) return;
-
-  const int kh = 8 * (lane >> 5);
-  const int bl = min(b0 + (lane & 31), a.B - 1);  // rows past B load row B-1, never stored
-  const __bf16* wp = a.W + ((long long)h * a.N + 32 * NT * ng + (lane & 31)) * K + kh;
-  const __bf16* xp = a.X + (long long)bl * a.x_row + (long long)h * a.x_head + kh;
+  const int bbase = 128 * blockIdx.y;
+  if (h >= a.H) return;  // uniform over the workgroup
+  const int n0 = kWRows * ng;
 
   f32x16 acc[NT];
 #pragma unroll
@@ -89,35 +96,80 @@ __global__ __launch_bounds__(256) void mla_head_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
-  bf16x8 fx[2][kBatch], fw[2][kBatch][NT];
-  auto load = [&](int buf, int j) {
+  for (int kc = 0; kc < K; kc += kKC) {
+    // stage: row q < kWRows is W row n0 + q, else X row bbase + q - kWRows
+    // (rows past B load row B - 1; their results are never stored)
+    i32x4 v[kLoads];
 #pragma unroll
-    for (int s = 0; s < kBatch; ++s) {
-      const int k = 16 * (kBatch * j + s);
-      fx[buf][s] = *reinterpret_cast<const bf16x8*>(xp + k);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        fw[buf][s][t] = *reinterpret_cast<const bf16x8*>(wp + (long long)32 * t * K + k);
+    for (int j = 0; j < kLoads; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c >> 4, c16 = c & 15;
+      const __bf16* src;
+      if (row < kWRows) {
+        src = a.W + ((long long)h * a.N + n0 + row) * K + kc + 8 * c16;
+      } else {
+        const int b = min(bbase + row - kWRows, a.B - 1);
+        src = a.X + (long long)b * a.x_row + (long long)h * a.x_head + kc + 8 * c16;
+      }
+      v[j] = *reinterpret_cast<const i32x4*>(src);
     }
-  };
-  load(0, 0);
+    if (kc > 0) __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
-  for (int j = 0; j < kBatches; ++j) {
-    if (j + 1 < kBatches) load((j + 1) & 1, j + 1);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < kLoads; ++j) {
+      const int c = tid + 256 * j;
+      *reinterpret_cast<i32x4*>(lds + lds_slot(c >> 4, c & 15)) = v[j];
+    }
+    __syncthreads();
+    // wave w: requests bbase + 32 w .. +31 (B operand), NT n-tiles (A)
+    const int xr = 32 * w + (lane & 31);
 #pragma unroll
-    for (int s = 0; s < kBatch; ++s)
+    for (int s = 0; s < kKC / 16; ++s) {
+      const int c16 = 2 * s + (lane >> 5);
+      const bf16x8 fb = *reinterpret_cast<const bf16x8*>(lx + lds_slot(xr, c16));
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j & 1][s][t], fx[j & 1][s], acc[t], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 fa = *reinterpret_cast<const bf16x8*>(lw + lds_slot(32 * t + (lane & 31), c16));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[t], 0, 0, 0);
+      }
+    }
   }
 
-  // the RoPE part rides along with group 0: 32 rows x 128 B per wave, all
-  // loads issued before the stores
-  bf16x8 rv[4];
-  const bool rope = a.R != nullptr && ng == 0;
-  if (rope) {
+  // acc[t][e] is Y^T[row 8(e/4) + 4(lane/32) + e%4, column lane%32] of tile t:
+  // four consecutive n of one request per group of four registers.  The
+  // workgroup's output block (128 requests x 32 NT values of n) goes through
+  // LDS, 16-byte chunk c of request row q at slot c ^ (q % (4 NT)), so that
+  // each request's 64 NT contiguous bytes are stored by consecutive lanes.
+  constexpr int kOutRow = 64 * NT;  // bytes per request row of the block
+  constexpr int kChunks = 4 * NT;   // 16-byte chunks per row
+  static_assert(128 * kOutRow <= (kWRows + kXRows) * kRowB, "output block fits the LDS");
+  auto out_slot = [&](int q, int c) { return q * kOutRow + 16 * (c ^ (q & (kChunks - 1))); };
+  __syncthreads();  // every fragment read is done
+  {
+    const int q = 32 * w + (lane & 31);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(acc[t][4 * g + e]);
+        *reinterpret_cast<bf16x4*>(lds + out_slot(q, 4 * t + g) + 8 * (lane >> 5)) = o;
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 128 * kChunks / 256; ++j) {
+    const int idx = tid + 256 * j;
+    const int q = idx / kChunks, c = idx % kChunks;
+    const int b = bbase + q;
+    if (b < a.B)
+      *reinterpret_cast<i32x4*>(a.Y + (long long)b * a.y_row + (long long)h * a.y_head + n0 + 8 * c) =
+          *reinterpret_cast<const i32x4*>(lds + out_slot(q, c));
+  }
+  // the RoPE part rides along with group 0: 32 rows x 128 B per wave
+  if (a.R != nullptr && ng == 0) {
+    const int b0 = bbase + 32 * w;
+    bf16x8 rv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = lane + 64 * j;
@@ -125,24 +177,6 @@ __global__ __launch_bounds__(256) void mla_head_gemm_kernel(GemmArgs a) {
       rv[j] = *reinterpret_cast<const bf16x8*>(a.R + (long long)row * a.r_row +
                                                (long long)h * a.r_head + 8 * (c & 7));
     }
-  }
-
-  // acc[t][e] is Y^T[row 8(e/4) + 4(lane/32) + e%4, column lane%32] of tile t:
-  // four consecutive n of one request per group of four registers
-  const int b = b0 + (lane & 31);
-  if (b < a.B) {
-    __bf16* yp = a.Y + (long long)b * a.y_row + (long long)h * a.y_head + 32 * NT * ng + 4 * (lane >> 5);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[t][4 * g + e]);
-        *reinterpret_cast<bf16x4*>(yp + 32 * t + 8 * g) = v;
-      }
-  }
-  if (rope) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = lane + 64 * j;
@@ -179,12 +213,12 @@ mla_status check_bh(int32_t B, int32_t H) {
   return MLA_OK;
 }
 
-template <int K, int NT, int KB>
+template <int K, int NT>
 mla_status launch_gemm(const GemmArgs& a, void* stream) {
   const int T = a.N / (32 * NT);
   const int groups = (a.H + 7) / 8;
   dim3 grid(8 * T * groups, (a.B + 127) / 128);
-  hipLaunchKernelGGL((mla_head_gemm_kernel<K, NT, KB>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL((mla_head_gemm_kernel<K, NT>), grid, dim3(256), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -223,7 +257,7 @@ mla_status mla_absorb_query(const void* q_in, const void* w_uk_t, void* q, int32
   a.R = static_cast<const __bf16*>(q_in) + kDN;
   a.r_row = (long long)H * kDQ;
   a.r_head = kDQ;
-  return launch_gemm<kDN, 4, 4>(a, stream);
+  return launch_gemm<kDN, 4>(a, stream);
 }
 
 mla_status mla_up_project(const void* out, const void* w_uv, void* o, int32_t B, int32_t H,
@@ -246,7 +280,7 @@ mla_status mla_up_project(const void* out, const void* w_uv, void* o, int32_t B,
   a.R = nullptr;
   a.r_row = 0;
   a.r_head = 0;
-  return launch_gemm<kDV, 2, 4>(a, stream);
+  return launch_gemm<kDV, 1>(a, stream);
 }
 
 }  // extern "C"
