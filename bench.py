@@ -156,7 +156,22 @@ def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
             "attend_frac_of_gemm": tflops / mm_tfs}
 
 
-def append_record(w, reps: int = 200) -> dict:
+def prewarm(fn, ms: float) -> int:
+    """Untimed calls of fn for about ms milliseconds (in batches of 10, each
+    synchronised), so that the timed calls after it run at the loaded clock;
+    returns the number of calls."""
+    import torch
+    n = 0
+    t_end = time.time() + ms * 1e-3
+    while time.time() < t_end:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def append_record(w, reps: int = 200, prewarm_ms: float = 0.0) -> dict:
     """The paged latent append (the step before decode) on the same cache: one
     new token per request, written over each request's last cached row after
     the timed decode steps.  HIP events around `reps` launches."""
@@ -167,6 +182,8 @@ def append_record(w, reps: int = 200) -> dict:
     new = torch.randn((w.B, 576), generator=g, device=dev).to(torch.bfloat16)
     pos = (w.seq_lens - 1).clamp(min=0).to(torch.int32)
     mla.append_latent(new[:, :512], new[:, 512:], pos, w.block_table, w.cache)
+    prewarm(lambda i: mla.append_latent(new[:, :512], new[:, 512:], pos, w.block_table, w.cache),
+            prewarm_ms)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -181,7 +198,7 @@ def append_record(w, reps: int = 200) -> dict:
             "gb_s": moved / t / 1e9}
 
 
-def absorb_record(B: int, H: int, reps: int = 100) -> dict:
+def absorb_record(B: int, H: int, reps: int = 100, prewarm_ms: float = 0.0) -> dict:
     """Query absorption and value up-projection at the decode's batch shape,
     with random weights of the layer's shape (W_UK, W_UV: [H, 128, 512] bf16).
     HIP events around `reps` launches of each; bytes are the weights plus the
@@ -200,6 +217,7 @@ def absorb_record(B: int, H: int, reps: int = 100) -> dict:
 
     def timed(fn):
         fn()
+        prewarm(lambda i: fn(), prewarm_ms)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -225,10 +243,11 @@ def absorb_record(B: int, H: int, reps: int = 100) -> dict:
     return res
 
 
-def fp8_record(w, layers_copies: int, steps: int, warmup: int) -> dict:
+def fp8_record(w, layers_copies: int, steps: int, warmup: int, prewarm_ms: float = 0.0) -> dict:
     """The same decode step over an FP8 (e4m3) copy of the workload's cache:
     fresh fp8 caches rotated like the bf16 ones, plan + attend per step, HIP
-    events around every attend launch."""
+    events around every attend launch, after the same pre-warm as the bf16
+    steps (building the fp8 caches leaves the GPU idle for a while)."""
     import torch
     import mla_latent_cache_absorbed_amd as mla
     from mla_latent_cache_absorbed_amd import accounting as acc
@@ -254,8 +273,9 @@ def fp8_record(w, layers_copies: int, steps: int, warmup: int) -> dict:
         if ev is not None:
             ev[1].record()
 
+    n_pre = prewarm(step, prewarm_ms)
     for i in range(warmup):
-        step(i)
+        step(n_pre + i)
     torch.cuda.synchronize()
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
@@ -263,7 +283,7 @@ def fp8_record(w, layers_copies: int, steps: int, warmup: int) -> dict:
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        step(warmup + i, pairs[i])
+        step(n_pre + warmup + i, pairs[i])
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / steps
@@ -417,9 +437,9 @@ def main():
     }
     if not args.no_extras:
         if H > 32 and BS >= 32 and name != "step61":
-            rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup)
-        rec["append"] = append_record(w0)
-        rec["absorb"] = absorb_record(B, H)
+            rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup, args.prewarm_ms)
+        rec["append"] = append_record(w0, prewarm_ms=args.prewarm_ms)
+        rec["absorb"] = absorb_record(B, H, prewarm_ms=args.prewarm_ms)
         rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

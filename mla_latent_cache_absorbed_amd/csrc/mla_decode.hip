@@ -61,6 +61,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 #define CONST_AS __attribute__((address_space(4)))
 
@@ -390,22 +391,23 @@ __device__ __forceinline__ void issue_one(const StageOne& s, char LDS_AS* sbuf, 
 // bytes, row-major as in memory (with blocks of 32 tokens or more a stage is
 // one contiguous 18,432-byte run of its block, so its 18 loads of 1 KB are
 // fully coalesced), except that the 16-byte chunk c of token t sits at slot
-// c ^ x8(t) of its row: x8(t) = (t >> 2) & 3 keeps c within its aligned
-// group of four, and spreads the score reads (lanes 0..31 read 8 bytes of
-// one chunk of tokens 0..31; the row stride is 576 = 9 * 64 bytes) over
-// distinct bank groups.  Score operands are converted to bf16 in registers;
-// each wave converts its own column slab of kv_c to bf16 into the V slot, in
-// the bf16 stage's region-A layout, where the weighted sum reads it exactly
-// as for a bf16 cache.  e4m3 values are exact in bf16, so the products are
-// the same as for a bf16 cache holding the dequantised values divided by
-// the scale; the scale multiplies the scores and the output.
+// c ^ x8(t) of its row.  x8(t) (two bits: bit 2 of t, and bit 3 xor bit 1)
+// keeps c within its aligned group of four and spreads both operand reads
+// over distinct banks (the row stride is 576 = 9 * 64 bytes):
+//   scores : lanes 0..31 read one 16-byte chunk of tokens 0..31 (lanes
+//            32..63 the next chunk), each read serving two k-steps;
+//   V^T    : ds_read_b64_tr_b8, each 16-lane group reads 8 tokens x 16
+//            bytes of one chunk, and each lane gets one column of 8 tokens.
+// Both operands are converted to bf16 in registers just before their MFMAs.
+// e4m3 values are exact in bf16, so the products are the same as for a bf16
+// cache holding the dequantised values divided by the scale; the scale
+// multiplies the scores and the output.
 // ---------------------------------------------------------------------------
 constexpr int kRow8 = kD;               // bytes per fp8 row
 constexpr int kStage8 = kSub * kRow8;   // 18,432 B
 constexpr int kLoads8 = kStage8 / 1024; // 18 loads of 1 KB per stage
-constexpr int kVSlot = kSub * 1024;     // bf16 kv_c of one stage
 
-__device__ __forceinline__ int x8(int t) { return (t >> 2) & 3; }
+__device__ __forceinline__ int x8(int t) { return ((t >> 2) & 1) | ((((t >> 3) ^ (t >> 1)) & 1) << 1); }
 
 // Load L (< 18) of a one-block fp8 stage: LDS bytes [1024 L, 1024 L + 1024).
 // Lane i's 16 bytes land at 1024 L + 16 i = row t, slot; they come from
@@ -415,7 +417,7 @@ __device__ __forceinline__ void issue_one8(const StageOne& s, char LDS_AS* sbuf,
   const uint32_t o = uint32_t(L) * 1024 + lane16;
   const uint32_t t = (o * 29128u) >> 24;  // o / 576, exact for o < 18,432
   const uint32_t slot = (o - t * kRow8) >> 4;
-  const uint32_t chunk = slot ^ ((t >> 2) & 3);
+  const uint32_t chunk = slot ^ uint32_t(x8(int(t)));
   dma16_plain(s.r, min(s.row0 + t * kRow8, s.rowlast) + chunk * 16, sbuf + L * 1024);
 }
 
@@ -438,25 +440,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 v) {
                                           (int)fp8x2_lo(v[1]), (int)fp8x2_hi(v[1])});
 }
 
-// Wave w's slab of kv_c (dims 512 w / NW .. +512 / NW) of an fp8 stage, to
-// bf16 in the V slot: lane l converts token l / 2, half l % 2 of the slab.
-template <int NW>
-__device__ __forceinline__ void convert_v8(const char LDS_AS* s8, char LDS_AS* vs, int w, int lane) {
-  constexpr int CH = 16 / NW;  // fp8 chunks per lane
-  const int t = lane >> 1;
-  const int c8 = (32 / NW) * w + CH * (lane & 1);
-  const int xt = x8(t), sa = swzA(t);
-  i32x4 raw[CH];
-#pragma unroll
-  for (int q = 0; q < CH; ++q) raw[q] = *(const i32x4 LDS_AS*)(s8 + t * kRow8 + 16 * (c8 + (q ^ xt)));
-#pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    const int cb = 2 * (c8 + q);  // bf16 chunks cb, cb + 1
-    *(bf16x8 LDS_AS*)(vs + t * 1024 + 16 * (cb ^ sa)) = fp8x8_to_bf16(u32x2{(uint32_t)raw[q][0], (uint32_t)raw[q][1]});
-    *(bf16x8 LDS_AS*)(vs + t * 1024 + 16 * ((cb + 1) ^ sa)) = fp8x8_to_bf16(u32x2{(uint32_t)raw[q][2], (uint32_t)raw[q][3]});
-  }
-}
-
 template <bool V>
 struct BoolC {
   static constexpr bool value = V;
@@ -473,20 +456,20 @@ struct Pick<false, A, B> {
 constexpr int kWaveBytesM = 32 * kDV * 4;  // one wave's share of an item's partial
 
 // kOne: the block size is 32 tokens or more, so every stage lies in one block.
-// kF8: the cache is fp8 (e4m3); stages hold fp8 rows and one more LDS slot
-// holds the bf16 kv_c of the stage being summed.
+// kF8: the cache is fp8 (e4m3); stages hold fp8 rows, whose operands are
+// converted in registers.
 template <int NW, int NS, bool kOne, bool kF8 = false>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   static_assert(NW == 2 || NW == 4, "waves per workgroup");
   static_assert(NS >= 3, "the pipeline reads two stages while one more loads");
   static_assert(!kF8 || kOne, "fp8 stages are loaded from one block");
   constexpr int kSB = kF8 ? kStage8 : kStageBytes;       // bytes of a ring stage
-  constexpr int kRing = NS * kSB + (kF8 ? kVSlot : 0);    // the ring (and the V slot)
+  constexpr int kRing = NS * kSB;                        // the stage ring
   // loads per wave per stage (fp8: 18 loads over NW waves, the last repeated)
   constexpr int LPW = kF8 ? (kLoads8 + NW - 1) / NW : kLoadsPerStage / NW;
-  // score operand reads in flight (fp8: raw 8-byte fragments, each
-  // converted just before its MFMA)
-  constexpr int PFK = 4;
+  // score operand reads in flight: bf16 k-steps, or fp8 16-byte reads of
+  // two k-steps each (converted just before their MFMAs)
+  constexpr int PFK = kF8 ? 2 : 4;
   constexpr int PFV = 2;                    // weighted-sum operand reads in flight
   constexpr int HP = NW * 32;               // heads covered by the workgroup
   constexpr int CPW = 16 / NW;              // 32-column blocks of O per wave
@@ -497,7 +480,6 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kRing + 2 * PBUF];
   char LDS_AS* lds = (char LDS_AS*)(lds_raw);
   char LDS_AS* const pw = lds + kRing;
-  char LDS_AS* const vslot = lds + NS * kSB;  // fp8 only
   float LDS_AS* const x_l = (float LDS_AS*)pw;          // [HP] row sums
   float LDS_AS* const x_lse = x_l + HP;                 // [HP] log2-domain log-sum-exps
   int LDS_AS* const s_vote = (int LDS_AS*)(x_lse + HP);  // [NW] redo votes
@@ -532,10 +514,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     for (int j = 0; j < 8; ++j) qk_off[j] = hl * 1024 + ((((2 * j) | hi)) ^ xa) * 16;
   }
   const int qkb = kRegionB + hi * 512 + hl * 16;
-  // fp8: k-step s reads 8 bytes of chunk s of token hl at qk8_off[s & 3] + 64 (s >> 2)
-  int qk8_off[4];
+  // fp8: read m (k-steps 2m, 2m + 1) takes chunk 2m + hi of token hl, at
+  // qk16_off[m & 1] + 64 (m >> 1); k-step 2m + e uses its bytes 8e .. 8e + 7.
+  int qk16_off[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) qk8_off[j] = hl * kRow8 + 16 * (j ^ x8(hl)) + 8 * hi;
+  for (int j = 0; j < 2; ++j) qk16_off[j] = hl * kRow8 + 16 * (((2 * j) | hi) ^ x8(hl));
   // Weighted sum.  Wave w owns columns 32 CPW w .. 32 CPW (w + 1) - 1 of O
   // for all HP heads: accumulator o[hb CPW + c] is O^T of the 32 columns of
   // block cb = CPW w + c for heads 32 hb .. 32 hb + 31.  So each wave reads
@@ -557,6 +540,20 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       for (int j = 0; j < 4; ++j)
         pv_off[e][j] = T * 1024 + (((4 * j) | cc) ^ sa) * 16 + 8 * u0 + 256 * (CPW / 4) * w;
     }
+  }
+  // fp8 V fragment f (kk, c as above): lane 16 g + i of the transposing
+  // read supplies token 16 kk + 4 (g >> 1) + tok(i >> 1) (tok(j) = j % 4 +
+  // 8 (j / 4)), bytes 8 (i & 1) .. +7 of chunk 2 cb + (g & 1); the read hands
+  // lane l column 32 cb + l % 32 of tokens 16 kk + 4 hi + tok(0..7), the
+  // tokens of the P fragment's lane.  Offset pv8_off[c & 1] + 64 (c >> 1) +
+  // 16 kk rows.
+  int pv8_off[2];
+  {
+    const int g = lane >> 4, i = lane & 15, j = i >> 1;
+    const int T = 4 * (g >> 1) + (j & 3) + 8 * (j >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      pv8_off[e] = T * kRow8 + 16 * (2 * CPW * w + (((2 * e) | (g & 1)) ^ x8(T))) + 8 * (i & 1);
   }
   // P fragment (hb, kk): the B operand of the weighted sum for heads of
   // block hb over token half kk, as wave hb's lanes hold it (head 32 hb +
@@ -627,26 +624,34 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     float la = 0.0f, lb = 0.0f;  // this lane's share of the row sum, in two chains
     bool first_pass = true;   // uniform: false on a redo
 
-    using KRaw = typename Pick<kF8, u32x2, bf16x8>::T;
+    // score operand read ahead: a bf16 k-step, or (fp8) 16 bytes of two
+    using KRaw = typename Pick<kF8, i32x4, bf16x8>::T;
     auto kread = [&](const char LDS_AS* sb, int s) -> KRaw {
-      if constexpr (kF8) return *(const u32x2 LDS_AS*)(sb + qk8_off[s & 3] + 64 * (s >> 2));
+      if constexpr (kF8) return *(const i32x4 LDS_AS*)(sb + qk16_off[s & 1] + 64 * (s >> 1));
       else
         return s < 32 ? *(const bf16x8 LDS_AS*)(sb + qk_off[s & 7] + 256 * (s >> 3))
                       : *(const bf16x8 LDS_AS*)(sb + qkb + 1024 * (s - 32));
     };
-    auto kcvt = [&](const KRaw& x) -> bf16x8 {
-      if constexpr (kF8) return fp8x8_to_bf16(x);
-      else return x;
+    // fp8 k-step s of the read held in x
+    auto kcvt = [&](const i32x4& x, int s) -> bf16x8 {
+      return fp8x8_to_bf16(u32x2{(uint32_t)x[2 * (s & 1)], (uint32_t)x[2 * (s & 1) + 1]});
     };
+    // weighted-sum operand read ahead: bf16, or (fp8) 8 raw bytes
+    using VRaw = typename Pick<kF8, u32x2, bf16x8>::T;
 #define MLA_VREAD(sb, f, dst)                                                               \
   do {                                                                                      \
     const int c_ = (f) % CPW, kk_ = (f) / CPW;                                              \
-    const int imm_ = kk_ * 16384 + 256 * (c_ >> 2);                                         \
-    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)((sb) + pv_off[0][c_ & 3] + imm_));                                 \
-    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)((sb) + pv_off[1][c_ & 3] + imm_));                                 \
-    dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
+    if constexpr (kF8) {                                                                    \
+      dst = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(               \
+          (i32x2 LDS_AS*)((sb) + pv8_off[c_ & 1] + 64 * (c_ >> 1) + kk_ * (16 * kRow8))));   \
+    } else {                                                                                \
+      const int imm_ = kk_ * 16384 + 256 * (c_ >> 2);                                       \
+      const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                          \
+          (bf16x4 LDS_AS*)((sb) + pv_off[0][c_ & 3] + imm_));                               \
+      const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                          \
+          (bf16x4 LDS_AS*)((sb) + pv_off[1][c_ & 3] + imm_));                               \
+      dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};         \
+    }                                                                                       \
   } while (0)
 #define MLA_PREAD(pb, hb, kk) (*(const bf16x8 LDS_AS*)((pb) + ((hb) * 2 + (kk)) * 1024 + p_lane))
 #define MLA_PWRITE(pb, kk, val) (*(bf16x8 LDS_AS*)((pb) + (w * 2 + (kk)) * 1024 + p_lane) = (val))
@@ -702,16 +707,18 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     };
     for (;;) {
       // Queries of this wave's 32 heads, as the B operand of the QK MFMA:
-      // lane holds head hl, dims 16s + 8hi .. +7 (reloaded on a redo so that
-      // they are not live past the last score MFMA of a pass).
+      // lane holds head hl, dims 16s + 8hi .. +7 for k-step s (fp8: dims
+      // 16 (2 (s >> 1) + hi) + 8 (s & 1) .. +7, the order of the 16-byte
+      // score reads), reloaded on a redo so that they are not live past the
+      // last score MFMA of a pass.
       // Lanes of padding heads load head 0's query (their results are never
       // written); no select follows the loads, so they all go out at once.
       bf16x8 qreg[36];
       {
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            a.q + (size_t(b) * a.H + (head_ok ? head : 0)) * kD + 8 * hi);
+            a.q + (size_t(b) * a.H + (head_ok ? head : 0)) * kD + (kF8 ? 16 : 8) * hi);
 #pragma unroll
-        for (int s = 0; s < 36; ++s) qreg[s] = qp[2 * s];
+        for (int s = 0; s < 36; ++s) qreg[s] = kF8 ? qp[4 * (s >> 1) + (s & 1)] : qp[2 * s];
       }
       // Stage 0 goes out behind the queries, and both are waited for before
       // the next stages go out: the compiler counts only its own (query)
@@ -741,8 +748,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
           if constexpr (kF8) {
-            const bf16x8 kb = kcvt(kf[s % PFK]);
-            if (s + PFK < 36) kf[s % PFK] = kread(sb, s + PFK);
+            const int m = s >> 1;
+            const bf16x8 kb = kcvt(kf[m % PFK], s);
+            if ((s & 1) && m + PFK < 18) kf[m % PFK] = kread(sb, m + PFK);
             if (s == 0) qk_first(sacc, kb, qreg[0]);
             else qk_next(sacc, kb, qreg[s]);
           } else {
@@ -755,7 +763,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       }
       // register v holds token 4hi + 8(v/4) + (v%4) of its stage: valid
       // while 8(v/4) + (v%4) < (stage end) - 4hi
-      bf16x8 vf[PFV];  // weighted-sum operands, read ahead
+      VRaw vf[PFV];  // weighted-sum operands, read ahead
       {
         const int lim = t1 - t0 - 4 * hi;
         if (first_pass) {
@@ -779,20 +787,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         }
         MLA_PWRITE(pw, 0, p0);
         MLA_PWRITE(pw, 1, p1);
-        if constexpr (kF8) {
-          convert_v8<NW>(lds, vslot, w, lane);
 #pragma unroll
-          for (int s = 0; s < PFV; ++s) MLA_VREAD(vslot, s, vf[s]);
-        } else {
-#pragma unroll
-          for (int s = 0; s < PFV; ++s) MLA_VREAD(lds, s, vf[s]);
-        }
+        for (int s = 0; s < PFV; ++s) MLA_VREAD(lds, s, vf[s]);
       }
 
       auto iteration = [&](int k, auto mask_tag) {
         constexpr bool kMask = decltype(mask_tag)::value;
         constexpr int kDmaEvery = 36 / LPW;  // score MFMAs per load issued
-        const char LDS_AS* sbv = kF8 ? vslot : lds + (k % NS) * kSB;
+        const char LDS_AS* sbv = lds + (k % NS) * kSB;
         const char LDS_AS* pcur = pw + (k & 1) * PBUF;
         char LDS_AS* pnxt = pw + ((k + 1) & 1) * PBUF;
         // stage k+1 and every wave's P(k) must be in LDS; stage k+2 may
@@ -816,9 +818,19 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         bf16x8 pa[NW], pb[NW];  // P(k) fragments of the two token halves
 #pragma unroll
         for (int h = 0; h < NW; ++h) pa[h] = MLA_PREAD(pcur, h, 0);
+        bf16x8 vcur;  // fp8: the V fragment in use, converted
         auto pv_step = [&](int n) {
           const int f = n / NW, h = n % NW;
-          pv_mfma(o[h * CPW + f % CPW], vf[f % PFV], n < 16 ? pa[h] : pb[h]);
+          if constexpr (kF8) {
+            if (h == 0) {
+              vcur = fp8x8_to_bf16(vf[f % PFV]);
+              pv_mfma_v(o[h * CPW + f % CPW], vcur, n < 16 ? pa[h] : pb[h]);
+            } else {
+              pv_mfma(o[h * CPW + f % CPW], vcur, n < 16 ? pa[h] : pb[h]);
+            }
+          } else {
+            pv_mfma(o[h * CPW + f % CPW], vf[f % PFV], n < 16 ? pa[h] : pb[h]);
+          }
           if (h == NW - 1 && f + PFV < 2 * CPW) MLA_VREAD(sbv, f + PFV, vf[f % PFV]);
           if (n >= 16 - NW && n < 16) pb[h] = MLA_PREAD(pcur, h, 1);
         };
@@ -826,8 +838,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
           if constexpr (kF8) {
-            const bf16x8 kb = kcvt(kf[s % PFK]);
-            if (s + PFK < 36) kf[s % PFK] = kread(sbk, s + PFK);
+            const int m = s >> 1;
+            const bf16x8 kb = kcvt(kf[m % PFK], s);
+            if ((s & 1) && m + PFK < 18) kf[m % PFK] = kread(sbk, m + PFK);
             if (s == 0) qk_first(sacc, kb, qreg[0]);
             else qk_next(sacc, kb, qreg[s]);
           } else {
@@ -857,34 +870,35 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
           if (v == 15) MLA_PWRITE(pnxt, 1, n1);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // operands of the next weighted sum (stage k+1, already in LDS; an
-        // fp8 stage's kv_c slab goes to the V slot first, after every read of
-        // stage k's)
-        if constexpr (kF8) {
-          asm volatile("" ::: "memory");
-          convert_v8<NW>(sbk, vslot, w, lane);
+        // operands of the next weighted sum (stage k+1, already in LDS)
 #pragma unroll
-          for (int s = 0; s < PFV; ++s) MLA_VREAD(vslot, s, vf[s]);
-        } else {
-#pragma unroll
-          for (int s = 0; s < PFV; ++s) MLA_VREAD(sbk, s, vf[s]);
-        }
+        for (int s = 0; s < PFV; ++s) MLA_VREAD(sbk, s, vf[s]);
       };
       for (int k = 0; k + 2 < nst; ++k) iteration(k, BoolC<false>{});
       if (nst >= 2) iteration(nst - 2, BoolC<true>{});
       {
         // weighted sum of the last stage, once every wave's weights are in
-        const char LDS_AS* sbv = kF8 ? vslot : lds + ((nst - 1) % NS) * kSB;
+        const char LDS_AS* sbv = lds + ((nst - 1) % NS) * kSB;
         const char LDS_AS* pcur = pw + ((nst - 1) & 1) * PBUF;
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         block_barrier();
         bf16x8 pa[NW], pb[NW];
 #pragma unroll
         for (int h = 0; h < NW; ++h) pa[h] = MLA_PREAD(pcur, h, 0);
+        bf16x8 vcur;  // fp8: the V fragment in use, converted
 #pragma unroll
         for (int n = 0; n < 32; ++n) {
           const int f = n / NW, h = n % NW;
-          pv_mfma(o[h * CPW + f % CPW], vf[f % PFV], n < 16 ? pa[h] : pb[h]);
+          if constexpr (kF8) {
+            if (h == 0) {
+              vcur = fp8x8_to_bf16(vf[f % PFV]);
+              pv_mfma_v(o[h * CPW + f % CPW], vcur, n < 16 ? pa[h] : pb[h]);
+            } else {
+              pv_mfma(o[h * CPW + f % CPW], vcur, n < 16 ? pa[h] : pb[h]);
+            }
+          } else {
+            pv_mfma(o[h * CPW + f % CPW], vf[f % PFV], n < 16 ? pa[h] : pb[h]);
+          }
           if (h == NW - 1 && f + PFV < 2 * CPW) MLA_VREAD(sbv, f + PFV, vf[f % PFV]);
           if (n >= 16 - NW && n < 16) pb[h] = MLA_PREAD(pcur, h, 1);
         }
@@ -1069,11 +1083,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       // of up to 36: every load of a round is in flight at once, and the
       // blocks land in LDS in the layout they were stored in.  The
       // log-sum-exps load meanwhile.
-      // (fp8: 32 KB per wave, within the ring and the V slot)
-      constexpr int kWaveBuf = kF8 ? 32 * 1024 : kStageBytes;
+      // (fp8: the ring's share of a wave, whole KB, at most 36 KB)
+      constexpr int kWB8 = kRing / NW / 1024 * 1024;
+      constexpr int kWaveBuf = (kF8 && kWB8 < kStageBytes) ? kWB8 : kStageBytes;
       static_assert(NW * kWaveBuf <= kRing, "merge staging fits the ring");
       char LDS_AS* mb = lds + w * kWaveBuf;
-      constexpr int kRound = kWaveBuf / 1024;  // 36 blocks (fp8: 32)
+      constexpr int kRound = kWaveBuf / 1024;  // 36 blocks (fp8: up to 36)
       constexpr int kBlocks = NW * CPW * 4;       // 64 blocks per wave
       auto blk_off = [&](int j) {  // block j = (h, c, g) of this wave's slab
         const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
@@ -2195,12 +2210,11 @@ mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache,
   const AttendArgs a = attend_args(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H,
                                    NB, BS, M, workspace);
   hipStream_t st = (hipStream_t)stream;
-  // six fp8 stages (two loading ahead of the four in flight) fill the LDS
-  // with the V slot and the weight buffers
+  // eight fp8 stages and the two weight buffers fill the 160 KiB of LDS
   if (pick_variant(H).nw == 4)
-    hipLaunchKernelGGL((mla_attend_kernel<4, 6, true, true>), dim3(ncu), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((mla_attend_kernel<4, 8, true, true>), dim3(ncu), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((mla_attend_kernel<2, 6, true, true>), dim3(ncu), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((mla_attend_kernel<2, 8, true, true>), dim3(ncu), dim3(128), 0, st, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -109,10 +109,18 @@ def test_fp8_ragged_full_size_sampled():
     _check(w, c8, wl.DEFAULT_KV_SCALE, "ragged sampled", requests=reqs)
 
 
-def test_fp8_matches_bf16_decode_of_dequantised_cache():
-    """The fp8 path equals the bf16 path over the dequantised cache (e4m3
-    values are exact in bf16; a power-of-two kv_scale keeps them exact)."""
-    w = _gpu(wl.make_custom([77, 1000, 3], H=128, BS=64, seed=12))
+@pytest.mark.parametrize("lens,H,BS", [([77, 1000, 3], 128, 64), ([2000, 45, 700, 1], 48, 32)])
+def test_fp8_matches_bf16_decode_of_dequantised_cache(lens, H, BS):
+    """The fp8 path against the bf16 path over the dequantised cache (e4m3
+    values are exact in bf16; a power-of-two kv_scale keeps them exact).
+
+    Every score product and every weighted-sum term is the same on both
+    paths; only the order in which the score MFMAs add up the 576 products
+    differs (the fp8 path reads two k-steps of 16 bytes at a time), which
+    moves a score by a few fp32 ulps.  So lse agrees to 1e-5 and each output
+    to one bf16 rounding step, 2^-7 of its magnitude (plus 1e-4 where terms
+    cancel)."""
+    w = _gpu(wl.make_custom(lens, H=H, BS=BS, seed=12))
     c8 = wl.fp8_cache(w.cache, 0.0625)
     deq = (c8.view(torch.float8_e4m3fn).float() * 0.0625).to(torch.bfloat16)
     o8, l8 = _run(w, c8, 0.0625)
@@ -121,10 +129,13 @@ def test_fp8_matches_bf16_decode_of_dequantised_cache():
     lb = torch.empty((w.B, w.H), dtype=torch.float32, device=DEV)
     mla.decode(wb.q, wb.cache, wb.block_table, wb.seq_lens, wb.scale, ob, lb)
     torch.cuda.synchronize()
-    # the same products and sums in the same order; the power-of-two scale
-    # only moves between the operands and the final factors, exactly
-    assert np.array_equal(o8, ob.float().cpu().numpy())
-    assert np.array_equal(l8, lb.cpu().numpy())
+    ob, lb = ob.float().cpu().numpy(), lb.cpu().numpy()
+    d_out = np.abs(o8 - ob)
+    d_lse = np.abs(l8 - lb)
+    _say(f"[fp8] vs bf16 of the dequantised cache: max |d out| {d_out.max():.3g}, "
+         f"equal {np.mean(o8 == ob):.4f}, max |d lse| {d_lse.max():.3g}")
+    assert np.all(d_out <= 2.0 ** -7 * np.maximum(np.abs(o8), np.abs(ob)) + 1e-4)
+    assert np.all(d_lse <= 1e-5 * np.maximum(1.0, np.abs(lb)))
 
 
 def test_fp8_scores_beyond_fp32_softmax_range_terminate():
