@@ -295,7 +295,8 @@ def fp8_record(w, layers_copies: int, steps: int, warmup: int, prewarm_ms: float
     gbs = alg_bytes / (att_avg * 1e-3) / 1e9
     tfs = alg_flops / (att_avg * 1e-3) / 1e12
     del caches
-    return {"kernel": "mla_attend_kernel<fp8>", "kv_scale": kv, "ms_per_step": ms_step,
+    return {"kernel": ("mla_attend_narrow_kernel<fp8>" if H <= 32 else "mla_attend_kernel<fp8>"),
+            "kv_scale": kv, "ms_per_step": ms_step,
             "value": acc.token_reads(seq) / (ms_step * 1e-3), "unit": "cached-token reads/s",
             "launch_ms": att_avg, "launch_ms_median": att[len(att) // 2], "launch_ms_min": att[0],
             "algorithmic_bytes_per_launch": alg_bytes, "achieved_gb_s": gbs,
@@ -436,7 +437,7 @@ def main():
         "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
     }
     if not args.no_extras:
-        if H > 32 and BS >= 32 and name != "step61":
+        if BS >= 32 and name != "step61":
             rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup, args.prewarm_ms)
         rec["append"] = append_record(w0, prewarm_ms=args.prewarm_ms)
         rec["absorb"] = absorb_record(B, H, prewarm_ms=args.prewarm_ms)

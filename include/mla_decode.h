@@ -154,7 +154,7 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
  *   out = kv_scale * sum_t softmax_t(s) * e4m3(c8_t[0:512])
  *
  * (e4m3 values are exact in bf16, so products are exact and accumulate in
- * fp32 as for a bf16 cache.)  Supported: 33 <= H <= 128 and BS >= 32
+ * fp32 as for a bf16 cache.)  Supported: 1 <= H <= 128 and BS >= 32
  * (otherwise MLA_ERR_UNSUPPORTED); kv_scale finite (else MLA_ERR_BAD_SCALE).
  * Everything else (plan, workspace, layouts of q, block_table, seq_lens,
  * out, lse, errors) is as for mla_decode / mla_decode_attend; the plan call

@@ -1300,12 +1300,20 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 // flight per compute unit) and none ever waits for another.  Splits are
 // merged as in the wide kernel, by wave: a request split in two by its last
 // item, wider splits by merge units of 128 columns.
+//
+// kF8: the cache is fp8 (e4m3, blocks of 32 tokens or more).  A stage is
+// then 18 KB, so a wave's slot holds two: while the wave computes stage st
+// from one half, stage st + 1 loads into the other, and the wave waits only
+// for loads issued a whole stage earlier.  Operands are read and converted
+// as in the wide kernel's fp8 path.
 // ---------------------------------------------------------------------------
 constexpr int kNarrowWaves = 4;
 constexpr int kNarrowUnits = 4;  // merge units per widely split request
 
-template <bool kOne>  // as for the wide kernel: every stage lies in one block
+template <bool kOne, bool kF8 = false>  // kOne as for the wide kernel: every stage lies in one block
 __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel(AttendArgs a) {
+  static_assert(!kF8 || kOne, "fp8 stages are loaded from one block");
+  static_assert(2 * kStage8 <= kStageBytes, "two fp8 stages fit a slot");
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNarrowWaves * kStageBytes];
   constexpr int PFK = 4;  // score operand reads in flight
   constexpr int PFV = 2;  // weighted-sum operand reads in flight
@@ -1353,18 +1361,36 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
       for (int j = 0; j < 4; ++j) pv_off[e][j] = T * 1024 + (((4 * j) | cc) ^ sa) * 16 + 8 * u0;
     }
   }
+  // fp8 offsets, as in the wide kernel's fp8 path with one wave owning all
+  // 16 column blocks: score read m at qk16_off[m & 1] + 64 (m >> 1); V
+  // fragment (cb, kk) at pv8_off[cb & 1] + 64 (cb >> 1) + 16 kk rows
+  int qk16_off[2], pv8_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) qk16_off[j] = hl * kRow8 + 16 * (((2 * j) | hi) ^ x8(hl));
+  {
+    const int g = lane >> 4, i = lane & 15, j = i >> 1;
+    const int T = 4 * (g >> 1) + (j & 3) + 8 * (j >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) pv8_off[e] = T * kRow8 + 16 * (((2 * e) | (g & 1)) ^ x8(T)) + 8 * (i & 1);
+  }
 #define MLA_KREAD(sb, s)                                                               \
   ((s) < 32 ? *(const bf16x8 LDS_AS*)((sb) + qk_off[(s) & 7] + 256 * ((s) >> 3))      \
             : *(const bf16x8 LDS_AS*)((sb) + qkb + 1024 * ((s) - 32)))
+#define MLA_KREAD16(sb, m) (*(const i32x4 LDS_AS*)((sb) + qk16_off[(m) & 1] + 64 * ((m) >> 1)))
 #define MLA_VREAD(sb, n, dst)                                                               \
   do {                                                                                      \
     const int cb_ = (n) & 15, kk_ = (n) >> 4;                                               \
-    const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                        \
-    const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)((sb) + pv_off[0][cb_ & 3] + imm_));                                \
-    const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                            \
-        (bf16x4 LDS_AS*)((sb) + pv_off[1][cb_ & 3] + imm_));                                \
-    dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};           \
+    if constexpr (kF8) {                                                                    \
+      dst = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(               \
+          (i32x2 LDS_AS*)((sb) + pv8_off[cb_ & 1] + 64 * (cb_ >> 1) + kk_ * (16 * kRow8)))); \
+    } else {                                                                                \
+      const int imm_ = kk_ * 16384 + 256 * (cb_ >> 2);                                      \
+      const bf16x4 lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                          \
+          (bf16x4 LDS_AS*)((sb) + pv_off[0][cb_ & 3] + imm_));                              \
+      const bf16x4 hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(                          \
+          (bf16x4 LDS_AS*)((sb) + pv_off[1][cb_ & 3] + imm_));                              \
+      dst = bf16x8{lo_[0], lo_[1], lo_[2], lo_[3], hi_[0], hi_[1], hi_[2], hi_[3]};         \
+    }                                                                                       \
   } while (0)
 
   // worker k takes item k directly, later items from the queue (as in the
@@ -1435,14 +1461,34 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
       {
         // padding heads load head 0's query (never written out); no select
         // follows the loads, so they all go out at once
+        // (fp8: in the order of the 16-byte score reads, as in the wide kernel)
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            a.q + (size_t(b) * a.H + (head_ok ? hl : 0)) * kD + 8 * hi);
+            a.q + (size_t(b) * a.H + (head_ok ? hl : 0)) * kD + (kF8 ? 16 : 8) * hi);
 #pragma unroll
-        for (int s = 0; s < 36; ++s) qreg[s] = qp[2 * s];
+        for (int s = 0; s < 36; ++s) qreg[s] = kF8 ? qp[4 * (s >> 1) + (s & 1)] : qp[2 * s];
+      }
+      if constexpr (kF8) {
+        // stage 0 into the first half (the query loads are older, so the
+        // first stage wait covers them too)
+        const StageOne id = stage_one<kRow8>(a, b, t0, t1, bad);
+#pragma unroll
+        for (int L = 0; L < kLoads8; ++L) issue_one8(id, slot, lane16, L);
       }
       for (int st = 0; st < nst; ++st) {
+        const char LDS_AS* cur = kF8 ? slot + (st & 1) * kStage8 : slot;
         // this wave's reads of the slot are done before it is refilled
-        if constexpr (kOne) {
+        if constexpr (kF8) {
+          if (st + 1 < nst) {
+            // the other half held stage st - 1, whose reads are done
+            const StageOne id = stage_one<kRow8>(a, b, t0 + (st + 1) * kSub, t1, bad);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int L = 0; L < kLoads8; ++L) issue_one8(id, slot + ((st + 1) & 1) * kStage8, lane16, L);
+            asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // stage st is in
+          } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+        } else if constexpr (kOne) {
           const StageOne id = stage_one(a, b, t0 + st * kSub, t1, bad);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -1453,9 +1499,23 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 #pragma unroll
           for (int j = 0; j < 36; ++j) issue_load<1>(a, id, slot, t1, 0, lane16, j);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (!kF8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         f32x16 sacc;
-        {
+        if constexpr (kF8) {
+          // 16-byte reads of two k-steps each, two reads ahead
+          i32x4 kq[2];
+          kq[0] = MLA_KREAD16(cur, 0);
+          kq[1] = MLA_KREAD16(cur, 1);
+#pragma unroll
+          for (int s = 0; s < 36; ++s) {
+            const int m = s >> 1;
+            const bf16x8 kb = fp8x8_to_bf16(u32x2{(uint32_t)kq[m & 1][2 * (s & 1)], (uint32_t)kq[m & 1][2 * (s & 1) + 1]});
+            if ((s & 1) && m + 2 < 18) kq[m & 1] = MLA_KREAD16(cur, m + 2);
+            if (s == 0) qk_mfma_first_v(sacc, kb, qreg[0]);
+            else qk_mfma_v(sacc, kb, qreg[s]);
+          }
+          qk_drain(sacc);
+        } else {
           bf16x8 kf[PFK];
 #pragma unroll
           for (int s = 0; s < PFK; ++s) kf[s] = MLA_KREAD(slot, s);
@@ -1490,13 +1550,14 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
           }
         }
         {
-          bf16x8 vf[PFV];
+          typename Pick<kF8, u32x2, bf16x8>::T vf[PFV];
 #pragma unroll
-          for (int s = 0; s < PFV; ++s) MLA_VREAD(slot, s, vf[s]);
+          for (int s = 0; s < PFV; ++s) MLA_VREAD(cur, s, vf[s]);
 #pragma unroll
           for (int s = 0; s < 32; ++s) {
-            pv_mfma_v(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
-            if (s + PFV < 32) MLA_VREAD(slot, s + PFV, vf[s % PFV]);
+            if constexpr (kF8) pv_mfma_v(o[s & 15], fp8x8_to_bf16(vf[s % PFV]), (s >> 4) ? p1 : p0);
+            else pv_mfma_v(o[s & 15], vf[s % PFV], (s >> 4) ? p1 : p0);
+            if (s + PFV < 32) MLA_VREAD(cur, s + PFV, vf[s % PFV]);
           }
         }
       }
@@ -1520,7 +1581,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 
     const float l_tot = pair_sum(la + lb);
     const float lse2 = m_run + log2f(l_tot);
-    const float own_inv = 1.0f / l_tot;
+    const float own_inv = (kF8 ? a.v_scale : 1.0f) / l_tot;
     if (cnt == 1) {
 #pragma unroll
       for (int cb = 0; cb < 16; ++cb)
@@ -1630,6 +1691,7 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
     }
   }
 #undef MLA_KREAD
+#undef MLA_KREAD16
 #undef MLA_VREAD
 
   // ---- merge units: 128 columns (16 blocks of 1 KB per item) each ----
@@ -2074,7 +2136,7 @@ mla_status validate_attend_fp8(const void* q, const void* latent_cache, const in
   mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
                                  workspace, workspace_bytes);
   if (s != MLA_OK) return s;
-  if (H <= 32 || BS < 32) return MLA_ERR_UNSUPPORTED;
+  if (BS < 32) return MLA_ERR_UNSUPPORTED;
   if (!isfinite(kv_scale)) return MLA_ERR_BAD_SCALE;
   return MLA_OK;
 }
@@ -2210,11 +2272,19 @@ mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache,
   const AttendArgs a = attend_args(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H,
                                    NB, BS, M, workspace);
   hipStream_t st = (hipStream_t)stream;
-  // eight fp8 stages and the two weight buffers fill the 160 KiB of LDS
-  if (pick_variant(H).nw == 4)
-    hipLaunchKernelGGL((mla_attend_kernel<4, 8, true, true>), dim3(ncu), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((mla_attend_kernel<2, 8, true, true>), dim3(ncu), dim3(128), 0, st, a);
+  // wide kernels: eight fp8 stages and the two weight buffers fill the 160
+  // KiB of LDS; narrow kernel (H <= 32): two fp8 stages per wave slot
+  switch (pick_variant(H).nw) {
+    case 4:
+      hipLaunchKernelGGL((mla_attend_kernel<4, 8, true, true>), dim3(ncu), dim3(256), 0, st, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((mla_attend_kernel<2, 8, true, true>), dim3(ncu), dim3(128), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL((mla_attend_narrow_kernel<true, true>), dim3(ncu), dim3(kNarrowWaves * 64), 0, st, a);
+      break;
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

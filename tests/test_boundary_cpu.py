@@ -169,12 +169,21 @@ def _decode8(**kw):
                                a["ws"], a["wsb"], a["stream"])
 
 
+def _no_device():
+    """True when no HIP device is visible: then a call whose arguments pass the
+    host checks stops at the first HIP call (MLA_ERR_HIP) instead of
+    launching on the fake pointers these tests use."""
+    import torch
+    return not torch.cuda.is_available()
+
+
 def test_fp8_decode_rejects_bad_arguments_on_host(L):
     assert _decode8(B=0) == _lib.MLA_OK
-    assert _decode8(H=32) == _lib.MLA_ERR_UNSUPPORTED     # the narrow kernel has no fp8 form
-    assert _decode8(H=1) == _lib.MLA_ERR_UNSUPPORTED
     assert _decode8(BS=16) == _lib.MLA_ERR_UNSUPPORTED    # fp8 stages load from one block
-    assert _decode8(H=33, BS=32) != _lib.MLA_ERR_UNSUPPORTED
+    if _no_device():
+        # every head count is supported (H <= 32 by the narrow kernel)
+        for H, BS in ((1, 64), (16, 64), (32, 32), (33, 32), (128, 256)):
+            assert _decode8(H=H, BS=BS) == _lib.MLA_ERR_HIP, (H, BS)
     assert _decode8(kv=float("nan")) == _lib.MLA_ERR_BAD_SCALE
     assert _decode8(kv=float("inf")) == _lib.MLA_ERR_BAD_SCALE
     assert _decode8(scale=float("nan")) == _lib.MLA_ERR_BAD_SCALE
@@ -183,7 +192,7 @@ def test_fp8_decode_rejects_bad_arguments_on_host(L):
     assert _decode8(cache=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
     assert _decode8(wsb=16) == _lib.MLA_ERR_WORKSPACE
     A = _lib.mla_decode_attend_fp8
-    assert A(FAKE, FAKE, FAKE, 0.1, 0.5, FAKE, FAKE, 2, 16, 14, 64, 7, FAKE, 1 << 40, None) \
+    assert A(FAKE, FAKE, FAKE, 0.1, 0.5, FAKE, FAKE, 2, 16, 14, 16, 7, FAKE, 1 << 40, None) \
         == _lib.MLA_ERR_UNSUPPORTED
     assert A(FAKE, FAKE, FAKE, 0.1, float("nan"), FAKE, FAKE, 2, 128, 14, 64, 7, FAKE, 1 << 40,
              None) == _lib.MLA_ERR_BAD_SCALE
