@@ -154,8 +154,9 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
  *   out = kv_scale * sum_t softmax_t(s) * e4m3(c8_t[0:512])
  *
  * (e4m3 values are exact in bf16, so products are exact and accumulate in
- * fp32 as for a bf16 cache.)  Supported: 1 <= H <= 128 and BS >= 32
- * (otherwise MLA_ERR_UNSUPPORTED); kv_scale finite (else MLA_ERR_BAD_SCALE).
+ * fp32 as for a bf16 cache.)  Supported: the head counts and block sizes of
+ * mla_decode (otherwise MLA_ERR_UNSUPPORTED); kv_scale finite (else
+ * MLA_ERR_BAD_SCALE).
  * Everything else (plan, workspace, layouts of q, block_table, seq_lens,
  * out, lse, errors) is as for mla_decode / mla_decode_attend; the plan call
  * is shared. */

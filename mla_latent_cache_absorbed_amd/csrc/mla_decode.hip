@@ -389,8 +389,8 @@ __device__ __forceinline__ void issue_one(const StageOne& s, char LDS_AS* sbuf, 
 // ---------------------------------------------------------------------------
 // FP8 latent (OCP e4m3, one scale per cache).  A stage holds 32 rows of 576
 // bytes, row-major as in memory (with blocks of 32 tokens or more a stage is
-// one contiguous 18,432-byte run of its block, so its 18 loads of 1 KB are
-// fully coalesced), except that the 16-byte chunk c of token t sits at slot
+// one contiguous 18,432-byte run of its block, with 16-token blocks two runs
+// of 9,216 bytes, so its 18 loads of 1 KB are fully coalesced), except that the 16-byte chunk c of token t sits at slot
 // c ^ x8(t) of its row.  x8(t) (two bits: bit 2 of t, and bit 3 xor bit 1)
 // keeps c within its aligned group of four and spreads both operand reads
 // over distinct banks (the row stride is 576 = 9 * 64 bytes):
@@ -419,6 +419,26 @@ __device__ __forceinline__ void issue_one8(const StageOne& s, char LDS_AS* sbuf,
   const uint32_t slot = (o - t * kRow8) >> 4;
   const uint32_t chunk = slot ^ uint32_t(x8(int(t)));
   dma16_plain(s.r, min(s.row0 + t * kRow8, s.rowlast) + chunk * 16, sbuf + L * 1024);
+}
+
+// Load L (< 18) of an fp8 stage over two blocks of 16 tokens (BS = 16).  A
+// block holds 16 rows = 9,216 bytes = 9 loads, so loads 0..8 read the first
+// block and loads 9..17 the second; rows past t1 read the last valid row,
+// which lies in the first block when the request ends there (then loads
+// 9..17 read it too).  The block of a load is therefore wave-uniform.
+__device__ __forceinline__ void issue_ids8(const AttendArgs& a, const StageIds& id, char LDS_AS* sbuf,
+                                           int t1, uint32_t lane16, int L) {
+  const int last = t1 - 1;
+  const uint32_t o = uint32_t(L) * 1024 + lane16;
+  const uint32_t t = (o * 29128u) >> 24;  // o / 576, exact for o < 18,432
+  const uint32_t slot = (o - t * kRow8) >> 4;
+  const uint32_t chunk = slot ^ uint32_t(x8(int(t)));
+  const bool second = L >= 9 && last >= id.base + 16;
+  const int tok0 = second ? id.base + 16 : id.base;  // first token of the block read
+  const int tok = min(id.base + int(t), last);
+  const __amdgpu_buffer_rsrc_t r =
+      block_rsrc(reinterpret_cast<const char*>(a.cache), second ? id.blk1 : id.blk0, 16 * kRow8);
+  dma16_plain(r, uint32_t(tok - tok0) * kRow8 + chunk * 16, sbuf + L * 1024);
 }
 
 // 8 e4m3 values (low byte first) to bf16, exactly: one packed conversion per
@@ -462,7 +482,6 @@ template <int NW, int NS, bool kOne, bool kF8 = false>
 __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   static_assert(NW == 2 || NW == 4, "waves per workgroup");
   static_assert(NS >= 3, "the pipeline reads two stages while one more loads");
-  static_assert(!kF8 || kOne, "fp8 stages are loaded from one block");
   constexpr int kSB = kF8 ? kStage8 : kStageBytes;       // bytes of a ring stage
   constexpr int kRing = NS * kSB;                        // the stage ring
   // loads per wave per stage (fp8: 18 loads over NW waves, the last repeated)
@@ -688,12 +707,13 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     auto stage_base = [&](int p) { return t0 + min(p, nst - 1) * kSub; };
     using Src = typename Pick<kOne, StageOne, StageIds>::T;
     auto src_of = [&](int base) -> Src {
-      if constexpr (kF8) return stage_one<kRow8>(a, b, base, t1, bad);
+      if constexpr (kF8 && kOne) return stage_one<kRow8>(a, b, base, t1, bad);
       else if constexpr (kOne) return stage_one(a, b, base, t1, bad);
       else return stage_ids(a, b, base, t1, bad);
     };
     auto issue = [&](const Src& sr, char LDS_AS* sbuf, int j) {
-      if constexpr (kF8) issue_one8(sr, sbuf, lane16, min(w + NW * j, kLoads8 - 1));
+      if constexpr (kF8 && kOne) issue_one8(sr, sbuf, lane16, min(w + NW * j, kLoads8 - 1));
+      else if constexpr (kF8) issue_ids8(a, sr, sbuf, t1, lane16, min(w + NW * j, kLoads8 - 1));
       else if constexpr (kOne) issue_one<NW>(sr, sbuf, w, lane_sw, rb_tok, rb_cp, j);
       else issue_load<NW>(a, sr, sbuf, t1, w, lane16, j);
     };
@@ -1301,7 +1321,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 // merged as in the wide kernel, by wave: a request split in two by its last
 // item, wider splits by merge units of 128 columns.
 //
-// kF8: the cache is fp8 (e4m3, blocks of 32 tokens or more).  A stage is
+// kF8: the cache is fp8 (e4m3).  A stage is
 // then 18 KB, so a wave's slot holds two: while the wave computes stage st
 // from one half, stage st + 1 loads into the other, and the wave waits only
 // for loads issued a whole stage earlier.  Operands are read and converted
@@ -1312,7 +1332,6 @@ constexpr int kNarrowUnits = 4;  // merge units per widely split request
 
 template <bool kOne, bool kF8 = false>  // kOne as for the wide kernel: every stage lies in one block
 __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel(AttendArgs a) {
-  static_assert(!kF8 || kOne, "fp8 stages are loaded from one block");
   static_assert(2 * kStage8 <= kStageBytes, "two fp8 stages fit a slot");
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNarrowWaves * kStageBytes];
   constexpr int PFK = 4;  // score operand reads in flight
@@ -1467,23 +1486,29 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 #pragma unroll
         for (int s = 0; s < 36; ++s) qreg[s] = kF8 ? qp[4 * (s >> 1) + (s & 1)] : qp[2 * s];
       }
-      if constexpr (kF8) {
-        // stage 0 into the first half (the query loads are older, so the
-        // first stage wait covers them too)
-        const StageOne id = stage_one<kRow8>(a, b, t0, t1, bad);
+      // an fp8 stage into the slot half at dst (this wave's 18 loads)
+      auto issue8 = [&](int base, char LDS_AS* dst) {
+        if constexpr (kOne) {
+          const StageOne id = stage_one<kRow8>(a, b, base, t1, bad);
 #pragma unroll
-        for (int L = 0; L < kLoads8; ++L) issue_one8(id, slot, lane16, L);
-      }
+          for (int L = 0; L < kLoads8; ++L) issue_one8(id, dst, lane16, L);
+        } else {
+          const StageIds id = stage_ids(a, b, base, t1, bad);
+#pragma unroll
+          for (int L = 0; L < kLoads8; ++L) issue_ids8(a, id, dst, t1, lane16, L);
+        }
+      };
+      // stage 0 into the first half (the query loads are older, so the
+      // first stage wait covers them too)
+      if constexpr (kF8) issue8(t0, slot);
       for (int st = 0; st < nst; ++st) {
         const char LDS_AS* cur = kF8 ? slot + (st & 1) * kStage8 : slot;
         // this wave's reads of the slot are done before it is refilled
         if constexpr (kF8) {
           if (st + 1 < nst) {
             // the other half held stage st - 1, whose reads are done
-            const StageOne id = stage_one<kRow8>(a, b, t0 + (st + 1) * kSub, t1, bad);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-            for (int L = 0; L < kLoads8; ++L) issue_one8(id, slot + ((st + 1) & 1) * kStage8, lane16, L);
+            issue8(t0 + (st + 1) * kSub, slot + ((st + 1) & 1) * kStage8);
             asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // stage st is in
           } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -2128,7 +2153,7 @@ mla_status validate_attend(const void* q, const void* latent_cache, const int32_
   return check_workspace(workspace, workspace_bytes, B, H);
 }
 
-// The fp8 cache runs on the wide kernels (H > 32) with blocks of 32 tokens or more.
+// The fp8 cache runs on every kernel and block size the bf16 cache does.
 mla_status validate_attend_fp8(const void* q, const void* latent_cache, const int32_t* block_table,
                                float scale, float kv_scale, const void* out, const float* lse,
                                int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
@@ -2136,7 +2161,6 @@ mla_status validate_attend_fp8(const void* q, const void* latent_cache, const in
   mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
                                  workspace, workspace_bytes);
   if (s != MLA_OK) return s;
-  if (BS < 32) return MLA_ERR_UNSUPPORTED;
   if (!isfinite(kv_scale)) return MLA_ERR_BAD_SCALE;
   return MLA_OK;
 }
@@ -2274,15 +2298,20 @@ mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache,
   hipStream_t st = (hipStream_t)stream;
   // wide kernels: eight fp8 stages and the two weight buffers fill the 160
   // KiB of LDS; narrow kernel (H <= 32): two fp8 stages per wave slot
+  // (blocks of 16 tokens: each stage spans two blocks)
+  const bool one = a.lgBS >= 5;
   switch (pick_variant(H).nw) {
     case 4:
-      hipLaunchKernelGGL((mla_attend_kernel<4, 8, true, true>), dim3(ncu), dim3(256), 0, st, a);
+      if (one) hipLaunchKernelGGL((mla_attend_kernel<4, 8, true, true>), dim3(ncu), dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((mla_attend_kernel<4, 8, false, true>), dim3(ncu), dim3(256), 0, st, a);
       break;
     case 2:
-      hipLaunchKernelGGL((mla_attend_kernel<2, 8, true, true>), dim3(ncu), dim3(128), 0, st, a);
+      if (one) hipLaunchKernelGGL((mla_attend_kernel<2, 8, true, true>), dim3(ncu), dim3(128), 0, st, a);
+      else hipLaunchKernelGGL((mla_attend_kernel<2, 8, false, true>), dim3(ncu), dim3(128), 0, st, a);
       break;
     default:
-      hipLaunchKernelGGL((mla_attend_narrow_kernel<true, true>), dim3(ncu), dim3(kNarrowWaves * 64), 0, st, a);
+      if (one) hipLaunchKernelGGL((mla_attend_narrow_kernel<true, true>), dim3(ncu), dim3(kNarrowWaves * 64), 0, st, a);
+      else hipLaunchKernelGGL((mla_attend_narrow_kernel<false, true>), dim3(ncu), dim3(kNarrowWaves * 64), 0, st, a);
       break;
   }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;

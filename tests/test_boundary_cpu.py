@@ -179,10 +179,12 @@ def _no_device():
 
 def test_fp8_decode_rejects_bad_arguments_on_host(L):
     assert _decode8(B=0) == _lib.MLA_OK
-    assert _decode8(BS=16) == _lib.MLA_ERR_UNSUPPORTED    # fp8 stages load from one block
+    assert _decode8(BS=8) == _lib.MLA_ERR_UNSUPPORTED     # as for bf16: BS is 16 .. 1024
+    assert _decode8(H=129) == _lib.MLA_ERR_UNSUPPORTED
     if _no_device():
-        # every head count is supported (H <= 32 by the narrow kernel)
-        for H, BS in ((1, 64), (16, 64), (32, 32), (33, 32), (128, 256)):
+        # every head count and block size of the bf16 decode (H <= 32 by the
+        # narrow kernel, BS = 16 with stages over two blocks)
+        for H, BS in ((1, 64), (16, 64), (16, 16), (32, 32), (33, 32), (128, 16), (128, 256)):
             assert _decode8(H=H, BS=BS) == _lib.MLA_ERR_HIP, (H, BS)
     assert _decode8(kv=float("nan")) == _lib.MLA_ERR_BAD_SCALE
     assert _decode8(kv=float("inf")) == _lib.MLA_ERR_BAD_SCALE
@@ -192,7 +194,7 @@ def test_fp8_decode_rejects_bad_arguments_on_host(L):
     assert _decode8(cache=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
     assert _decode8(wsb=16) == _lib.MLA_ERR_WORKSPACE
     A = _lib.mla_decode_attend_fp8
-    assert A(FAKE, FAKE, FAKE, 0.1, 0.5, FAKE, FAKE, 2, 16, 14, 16, 7, FAKE, 1 << 40, None) \
+    assert A(FAKE, FAKE, FAKE, 0.1, 0.5, FAKE, FAKE, 2, 16, 14, 8, 7, FAKE, 1 << 40, None) \
         == _lib.MLA_ERR_UNSUPPORTED
     assert A(FAKE, FAKE, FAKE, 0.1, float("nan"), FAKE, FAKE, 2, 128, 14, 64, 7, FAKE, 1 << 40,
              None) == _lib.MLA_ERR_BAD_SCALE

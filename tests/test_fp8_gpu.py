@@ -63,10 +63,11 @@ def test_fp8_heads(H):
     _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"H={H}")
 
 
-@pytest.mark.parametrize("H", [128, 16])
-@pytest.mark.parametrize("BS", [32, 64, 128, 256])
+@pytest.mark.parametrize("H", [128, 48, 16])
+@pytest.mark.parametrize("BS", [16, 32, 64, 128, 256])
 def test_fp8_block_sizes(BS, H):
-    w = _gpu(wl.make_custom([5, 95, 300, 1000], H=H, BS=BS, seed=BS + H, poison_unused=True))
+    """BS = 16 stages span two blocks (a request may end in the first)."""
+    w = _gpu(wl.make_custom([5, 95, 300, 1000, 16, 17, 48], H=H, BS=BS, seed=BS + H, poison_unused=True))
     _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"BS={BS}")
 
 
@@ -78,9 +79,10 @@ def test_fp8_scales(kv):
 
 @pytest.mark.parametrize("H,chunk", [(128, 32), (128, 96), (128, 1024), (48, 64), (48, 1024),
                                      (16, 32), (16, 96), (16, 1024), (1, 64)])
-def test_fp8_forced_splits(H, chunk):
+@pytest.mark.parametrize("BS", [32, 16])
+def test_fp8_forced_splits(H, chunk, BS):
     """Splits of two and of three or more items: partials carry the scale."""
-    w = _gpu(wl.make_custom([2000, 45, 700, 1], H=H, BS=32, seed=chunk, poison_unused=True))
+    w = _gpu(wl.make_custom([2000, 45, 700, 1], H=H, BS=BS, seed=chunk, poison_unused=True))
     _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"H={H} chunk={chunk}", chunk=chunk)
 
 
@@ -95,6 +97,13 @@ def test_fp8_large_score_range_redo_path(H):
     c[blk, 500 % 64, :512] = torch.sign(q[0, 0, :512]) * 25.0  # 400 in e4m3 units at 1/16
     w = _gpu(wl.Workload(w.name, w.q, c.to(torch.bfloat16), w.block_table, w.seq_lens, w.scale))
     _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, "redo path")
+
+
+def test_fp8_tiny_configuration():
+    """The tiny parity shape (2 requests of 64 and 100 tokens, 128 heads,
+    16-token blocks) with an fp8 cache, checked in full."""
+    w = wl.make("tiny", device=DEV, seed=0)
+    _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, "tiny")
 
 
 def test_fp8_full_size_dp_rank_sampled():
