@@ -119,7 +119,7 @@ def decode_fp8(q: torch.Tensor, latent_cache_fp8: torch.Tensor, block_table: tor
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                workspace: Optional[Workspace] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Absorbed MLA decode over an FP8 (e4m3) latent cache whose values are
-    kv_scale * e4m3(byte); 33 <= H <= 128 and blocks of 32 tokens or more."""
+    kv_scale * e4m3(byte); the same head counts and block sizes as decode()."""
     _check_fp8_inputs(q, latent_cache_fp8, block_table, seq_lens)
     B, H, _ = q.shape
     NB, BS, _ = latent_cache_fp8.shape
