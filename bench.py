@@ -117,9 +117,21 @@ def cpu_baseline(w, budget_s: float):
         done_req += 1
     passes = done_req / w.B
     return {"value": done_tokens / elapsed, "unit": "cached-token reads/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"{done_req} request decodes ({passes:.1f} passes over the {w.B} requests, "
                       f"{done_tokens} tokens x {w.H} heads), float64 NumPy, {elapsed:.1f} s"}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
