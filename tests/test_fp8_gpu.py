@@ -174,3 +174,14 @@ def test_fp8_scores_beyond_fp32_softmax_range_terminate(H):
     flags = ws.check_flags()
     _say(f"[fp8] huge scale: flags {flags}")
     assert flags & ~mla._lib.MLA_CHECK_SCORE_RANGE == 0
+
+
+@pytest.mark.parametrize("H", [128, 16])
+@pytest.mark.parametrize("kv", [0.0, -0.25])
+def test_fp8_zero_and_negative_cache_scale(H, kv):
+    """kv_scale = 0 makes every cached value 0 (out = 0, lse = ln L); a
+    negative scale negates the cache, so both scores and output change sign
+    as the oracle's dequantised values do."""
+    w = _gpu(wl.make_custom([1, 70, 333, 2000], H=H, BS=64, seed=32, poison_unused=True))
+    c8 = wl.fp8_cache(w.cache, abs(kv) if kv != 0.0 else 0.0625)
+    _check(w, c8, kv, f"H={H} kv_scale={kv}")

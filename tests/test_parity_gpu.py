@@ -313,3 +313,20 @@ def test_full_size_sampled(name, reqs):
         reqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
     ro, rl = _sampled_oracle(w, reqs)
     _assert_parity(o[reqs], l[reqs], ro, rl, f"{name} requests {reqs}")
+
+
+@pytest.mark.parametrize("H", [128, 16])
+@pytest.mark.parametrize("scale", [0.0, -0.072, 0.5])
+def test_degenerate_and_negative_scales(H, scale):
+    """scale = 0 weighs every cached token equally (out is the mean of the
+    kv_c rows, lse = ln L); a negative scale reverses the scores; 0.5 gives
+    sharply peaked weights.  Wide (128 heads) and narrow (16 heads) kernels,
+    with a forced split so that the merge sees these weights too."""
+    w = wl.make_custom([1, 70, 333, 2000], H=H, BS=64, seed=31, poison_unused=True)
+    w = _to_gpu(wl.Workload(w.name, w.q, w.cache, w.block_table, w.seq_lens, float(np.float32(scale))))
+    for chunk in (None, 256):
+        out, lse = _run(w, chunk_tokens=chunk)
+        ro, rl = _oracle(w)
+        _assert_parity(out, lse, ro, rl, f"H={H} scale={scale} chunk={chunk}")
+    if scale == 0.0:
+        assert np.allclose(lse, np.log(np.asarray([1, 70, 333, 2000], dtype=np.float64))[:, None], atol=1e-5)
