@@ -64,7 +64,7 @@ def test_fp8_heads(H):
 
 
 @pytest.mark.parametrize("H", [128, 48, 16])
-@pytest.mark.parametrize("BS", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("BS", [16, 32, 64, 128, 256, 1024])
 def test_fp8_block_sizes(BS, H):
     """BS = 16 stages span two blocks (a request may end in the first)."""
     w = _gpu(wl.make_custom([5, 95, 300, 1000, 16, 17, 48], H=H, BS=BS, seed=BS + H, poison_unused=True))

@@ -80,9 +80,9 @@ def test_ragged_heads(H):
     _assert_parity(out, lse, ro, rl, f"ragged H={H}")
 
 
-@pytest.mark.parametrize("BS", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("BS", [16, 32, 64, 128, 256, 512, 1024])
 def test_block_sizes(BS):
-    lens = [5, 16, 48, 129, 300, 777]
+    lens = [5, 16, 48, 129, 300, 777, 2500]
     w = _to_gpu(wl.make_custom(lens, H=128, BS=BS, seed=BS, poison_unused=True))
     out, lse = _run(w)
     ro, rl = _oracle(w)
