@@ -278,6 +278,60 @@ def oracle_append(latent_cache: np.ndarray, block_table: np.ndarray,
     return cache, skipped
 
 
+def e4m3_from_f32(x) -> np.ndarray:
+    """Encode fp32 values as OCP FP8 E4M3 bytes: the finite code nearest to
+    the value, ties to the code with an even mantissa (round to nearest
+    even), magnitudes past 448 saturating to +-448 (S.1111.110), NaN to
+    0x7F, and the sign kept (-0 is 0x80).
+
+    Found by searching the 127 non-negative finite codes in order of
+    magnitude, which the decoding above defines; a tie sits exactly halfway
+    between two neighbouring codes, and of two neighbours the even code is
+    the one whose last bit (the mantissa's last bit) is 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mags = e4m3_to_f64(np.arange(0x7F))        # codes 0x00 .. 0x7E, ascending
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat_x, flat_o = x.reshape(-1), out.reshape(-1)
+    for i, v in enumerate(flat_x):
+        if np.isnan(v):
+            flat_o[i] = 0x7F
+            continue
+        a = abs(v)
+        j = int(np.searchsorted(mags, a))      # first code with magnitude >= a
+        if j >= len(mags):
+            c = 0x7E                           # past 448: saturate
+        elif mags[j] == a or j == 0:
+            c = j
+        else:
+            d_lo, d_hi = a - mags[j - 1], mags[j] - a
+            c = j - 1 if d_lo < d_hi else j if d_hi < d_lo else (j - 1 if (j - 1) % 2 == 0 else j)
+        flat_o[i] = c | (0x80 if np.signbit(v) else 0)
+    return out
+
+
+def oracle_append_fp8(cache_fp8: np.ndarray, block_table: np.ndarray, positions: Sequence[int],
+                      kv_c: np.ndarray, k_rope: np.ndarray, kv_scale: float
+                      ) -> Tuple[np.ndarray, int]:
+    """oracle_append for an FP8 cache [NB, BS, 576] of e4m3 bytes holding
+    values kv_scale * e4m3(byte): each bf16 input value v is stored as
+    e4m3_from_f32(fp32(v) / fp32(kv_scale)), the quotient rounded once to
+    fp32.  The page on TP sharding prices the FP8 cache (page "MLA 的 TP
+    切分…", sections 2.3 and 5.1) without a scale convention; this is the
+    inverse of the one the FP8 decode reads with.  Slots, skips and order are
+    those of oracle_append.
+    """
+    s32 = np.float32(kv_scale)
+
+    def quant(bits):
+        v = bf16_bits_to_f64(np.asarray(bits, dtype=np.uint16)).astype(np.float32)
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            return e4m3_from_f32((v / s32).astype(np.float64))
+    q_kv = [quant(np.asarray(kv_c[b])[:D_KVC]) for b in range(len(positions))]
+    q_kr = [quant(np.asarray(k_rope[b])[:D_ROPE]) for b in range(len(positions))]
+    return oracle_append(cache_fp8, block_table, positions, q_kv, q_kr)
+
+
 # ---------------------------------------------------------------------------
 # the explicit (non-absorbed) form, for checking the absorbed rewrite
 # ---------------------------------------------------------------------------
