@@ -55,6 +55,22 @@ mla_status mla_append_latent(const void* kv_c, int32_t kv_c_stride,
                              void* latent_cache, int32_t* skipped,
                              int32_t B, int32_t NB, int32_t BS, int32_t M, void* stream);
 
+/* The same append into an FP8 latent cache [NB, BS, 576] of OCP e4m3 bytes
+ * holding the values kv_scale * e4m3(byte), as mla_decode_fp8 reads it (page
+ * "MLA 的 TP 切分：为什么 8 张 GPU 存了同一份 KV cache", sections 2.3 and 5.1
+ * price the FP8 cache; they give no scale convention).  Each bf16 input
+ * value v is stored as the e4m3 code nearest to fp32(v) / kv_scale (the
+ * quotient correctly rounded to fp32, then rounded to the nearest code with
+ * ties to the even mantissa), magnitudes past 448 saturated to +-448 and NaN
+ * stored as 0x7F.  kv_scale must be finite and non-zero (else
+ * MLA_ERR_BAD_SCALE); every other argument, check and error is as for
+ * mla_append_latent, with latent_cache_fp8 16-byte aligned. */
+mla_status mla_append_latent_fp8(const void* kv_c, int32_t kv_c_stride,
+                                 const void* k_rope, int32_t k_rope_stride,
+                                 const int32_t* positions, const int32_t* block_table,
+                                 void* latent_cache_fp8, float kv_scale, int32_t* skipped,
+                                 int32_t B, int32_t NB, int32_t BS, int32_t M, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

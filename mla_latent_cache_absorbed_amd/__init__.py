@@ -20,6 +20,7 @@ from . import _lib
 from ._lib import MlaError  # noqa: F401
 
 __all__ = ["decode", "Workspace", "plan", "attend", "decode_fp8", "attend_fp8", "append_latent",
+           "append_latent_fp8",
            "absorb_prepare", "absorb_query", "up_project", "MlaError"]
 
 
@@ -165,17 +166,11 @@ def attend(q, latent_cache, block_table, scale, out, lse, workspace: Workspace) 
     _lib._check("mla_decode_attend", st)
 
 
-def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Tensor,
-                  block_table: torch.Tensor, latent_cache: torch.Tensor,
-                  skipped: Optional[torch.Tensor] = None) -> None:
-    """Store each request's new token (kv_c [B, >=512], k_rope [B, >=64], bf16 rows
-    with unit inner stride) at its position in the paged latent cache.
-    positions [B] int32 (negative: no token); skipped: optional int32 [1]
-    device counter of requests that could not be written."""
+def _check_append_args(kv_c, k_rope, positions, block_table, cache, cache_dtype, skipped):
     if kv_c.dtype != torch.bfloat16 or k_rope.dtype != torch.bfloat16:
         raise TypeError("kv_c and k_rope must be bfloat16")
-    if latent_cache.dtype != torch.bfloat16 or latent_cache.dim() != 3 or latent_cache.shape[2] != 576:
-        raise ValueError("latent_cache must be bfloat16 [NB, BS, 576]")
+    if cache.dtype != cache_dtype or cache.dim() != 3 or cache.shape[2] != 576:
+        raise ValueError(f"the cache must be {cache_dtype} [NB, BS, 576]")
     if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
         raise TypeError("positions and block_table must be int32")
     B = positions.shape[0]
@@ -185,10 +180,21 @@ def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Ten
         raise ValueError("kv_c rows need 512 and k_rope rows 64 contiguous elements")
     if block_table.dim() != 2 or block_table.shape[0] != B or not block_table.is_contiguous():
         raise ValueError("block_table must be a contiguous [B, M] tensor")
-    if not (latent_cache.is_contiguous() and positions.is_contiguous()):
-        raise ValueError("latent_cache and positions must be contiguous")
+    if not (cache.is_contiguous() and positions.is_contiguous()):
+        raise ValueError("the cache and positions must be contiguous")
     if skipped is not None and (skipped.dtype != torch.int32 or skipped.numel() < 1):
         raise TypeError("skipped must be an int32 device tensor")
+
+
+def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Tensor,
+                  block_table: torch.Tensor, latent_cache: torch.Tensor,
+                  skipped: Optional[torch.Tensor] = None) -> None:
+    """Store each request's new token (kv_c [B, >=512], k_rope [B, >=64], bf16 rows
+    with unit inner stride) at its position in the paged latent cache.
+    positions [B] int32 (negative: no token); skipped: optional int32 [1]
+    device counter of requests that could not be written."""
+    _check_append_args(kv_c, k_rope, positions, block_table, latent_cache, torch.bfloat16, skipped)
+    B = positions.shape[0]
     NB, BS, _ = latent_cache.shape
     M = block_table.shape[1]
     st = _lib.mla_append_latent(kv_c.data_ptr(), kv_c.stride(0), k_rope.data_ptr(), k_rope.stride(0),
@@ -197,6 +203,24 @@ def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Ten
                                 skipped.data_ptr() if skipped is not None else None,
                                 B, NB, BS, M, _stream())
     _lib._check("mla_append_latent", st)
+
+
+def append_latent_fp8(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Tensor,
+                      block_table: torch.Tensor, latent_cache_fp8: torch.Tensor, kv_scale: float,
+                      skipped: Optional[torch.Tensor] = None) -> None:
+    """append_latent into an FP8 cache (uint8 [NB, BS, 576] of e4m3 bytes
+    holding kv_scale * e4m3(byte)): each value is stored as the nearest e4m3
+    code to value / kv_scale (ties to even), saturated to +-448."""
+    _check_append_args(kv_c, k_rope, positions, block_table, latent_cache_fp8, torch.uint8, skipped)
+    B = positions.shape[0]
+    NB, BS, _ = latent_cache_fp8.shape
+    M = block_table.shape[1]
+    st = _lib.mla_append_latent_fp8(kv_c.data_ptr(), kv_c.stride(0), k_rope.data_ptr(), k_rope.stride(0),
+                                    positions.data_ptr(), block_table.data_ptr(),
+                                    latent_cache_fp8.data_ptr(), float(kv_scale),
+                                    skipped.data_ptr() if skipped is not None else None,
+                                    B, NB, BS, M, _stream())
+    _lib._check("mla_append_latent_fp8", st)
 
 
 def _bf16_contig(name, t, shape):

@@ -42,6 +42,7 @@ SIGNATURES = {
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_decode_abi_version": (_I, []),
     "mla_append_latent": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "mla_append_latent_fp8": (_I, [_P, _I, _P, _I, _P, _P, _P, _F, _P, _I, _I, _I, _I, _P]),
     "mla_decode_fp8": (_I, [_P, _P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_decode_attend_fp8": (_I, [_P, _P, _P, _F, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_absorb_prepare": (_I, [_P, _P, _I, _P]),
@@ -122,6 +123,13 @@ def mla_append_latent(kv_c, kv_c_stride, k_rope, k_rope_stride, positions, block
                       latent_cache, skipped, B, NB, BS, M, stream) -> int:
     return lib().mla_append_latent(kv_c, kv_c_stride, k_rope, k_rope_stride, positions,
                                    block_table, latent_cache, skipped, B, NB, BS, M, stream)
+
+
+def mla_append_latent_fp8(kv_c, kv_c_stride, k_rope, k_rope_stride, positions, block_table,
+                          latent_cache_fp8, kv_scale, skipped, B, NB, BS, M, stream) -> int:
+    return lib().mla_append_latent_fp8(kv_c, kv_c_stride, k_rope, k_rope_stride, positions,
+                                       block_table, latent_cache_fp8, kv_scale, skipped, B, NB, BS,
+                                       M, stream)
 
 
 def mla_absorb_prepare(w_uk, w_uk_t, H, stream) -> int:

@@ -132,3 +132,76 @@ def test_decode_loop_against_oracle():
         r = orc.parity_report(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl)
         _say(f"[append] decode loop step {step} lens {cur}: {r}")
         assert r["ok"], r
+
+
+def _check8(cache0, table, pos, buf, kv, kr, kv_scale, what):
+    cache = cache0.clone()
+    skipped = torch.zeros(1, dtype=torch.int32, device=DEV)
+    mla.append_latent_fp8(kv, kr, pos, table, cache, kv_scale, skipped)
+    torch.cuda.synchronize()
+    bb = _bits(buf)
+    want, n_skip = orc.oracle_append_fp8(cache0.cpu().numpy(), table.cpu().numpy(), pos.cpu().tolist(),
+                                         bb[:, :512], bb[:, 512:576], kv_scale)
+    got = cache.cpu().numpy()
+    diff = int((got != want).any(axis=-1).sum())
+    _say(f"[append fp8] {what}: rows differing {diff}, skipped {int(skipped.item())} (oracle {n_skip})")
+    assert diff == 0, what
+    assert int(skipped.item()) == n_skip, what
+
+
+@pytest.mark.parametrize("BS", [16, 64])
+@pytest.mark.parametrize("kv_scale", [0.0625, 0.3, -2.0])
+def test_append_fp8_bitwise(BS, kv_scale):
+    """The whole fp8 cache byte for byte against the oracle: random values,
+    exact midpoints between e4m3 codes (ties to even), values that saturate,
+    NaN, negative zero and subnormal codes, a skipped request and one with no
+    token."""
+    gen = torch.Generator().manual_seed(BS + int(abs(kv_scale) * 100))
+    B, M = 9, 5
+    NB = B * M + 2
+    table = torch.randperm(NB - 1, generator=gen)[: B * M].reshape(B, M).to(torch.int32)
+    table[7, 2] = NB + 5                       # a block id outside the cache
+    cache0 = torch.randint(0, 256, (NB, BS, 576), generator=gen, dtype=torch.uint8)
+    pos = torch.randint(0, M * BS, (B,), generator=gen, dtype=torch.int32)
+    pos[7] = 2 * BS + 1                        # lands on the bad block: skipped
+    pos[8] = -1                                # no token
+    buf = (torch.randn((B, 576), generator=gen) * 4 * abs(kv_scale)).to(torch.bfloat16)
+    codes = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    mids = (codes[1:] + codes[:-1]) / 2
+    special = torch.cat([mids, -mids, torch.tensor([449.0, 500.0, 1e4, -1e4, float("inf"), float("nan"),
+                                                      -0.0, 2.0 ** -9, 3 * 2.0 ** -10])])
+    buf[0, : special.numel()] = (special * kv_scale).to(torch.bfloat16)
+    buf = buf.to(DEV)
+    _check8(cache0.to(DEV), table.to(DEV), pos.to(DEV), buf, buf[:, :512], buf[:, 512:576], kv_scale,
+            f"BS={BS} kv_scale={kv_scale}")
+
+
+def test_fp8_decode_loop_against_oracle():
+    """Three decode steps over an fp8 cache: append each request's token (fp8),
+    decode over the longer sequences, against the oracle doing the same."""
+    gen = torch.Generator().manual_seed(5)
+    lens = [15, 64, 1, 0, 100]
+    kv = 0.0625
+    for H in (128, 16):
+        w = wl.make_custom([L + 3 for L in lens], H=H, BS=32, seed=6, poison_unused=True)
+        c8 = wl.fp8_cache(w.cache, kv).to(DEV)
+        table_d = w.block_table.to(DEV)
+        ref_cache = c8.cpu().numpy()
+        table = w.block_table.numpy()
+        cur = list(lens)
+        q = w.q.to(DEV)
+        for step in range(3):
+            buf, k_c, k_r = _new_tokens(w.B, gen)
+            mla.append_latent_fp8(k_c, k_r, torch.tensor(cur, dtype=torch.int32, device=DEV), table_d, c8, kv)
+            bb = _bits(buf)
+            ref_cache, n_skip = orc.oracle_append_fp8(ref_cache, table, cur, bb[:, :512], bb[:, 512:576], kv)
+            assert n_skip == 0
+            cur = [L + 1 for L in cur]
+            out, lse = mla.decode_fp8(q, c8, table_d, torch.tensor(cur, dtype=torch.int32, device=DEV),
+                                      w.scale, kv)
+            torch.cuda.synchronize()
+            assert np.array_equal(c8.cpu().numpy(), ref_cache), (H, step)
+            ro, rl = orc.oracle_decode_fp8(_bits(q), ref_cache, table, np.asarray(cur), w.scale, kv)
+            r = orc.parity_report(out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl)
+            _say(f"[append fp8] decode loop H={H} step {step}: {r}")
+            assert r["ok"], r

@@ -227,3 +227,27 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def _append8(**kw):
+    a = dict(kv=FAKE, kvs=576, kr=FAKE + 1024, krs=576, pos=FAKE, table=FAKE, cache=FAKE, kvsc=0.0625,
+             skipped=None, B=4, NB=14, BS=16, M=7, stream=None)
+    a.update(kw)
+    return _lib.mla_append_latent_fp8(a["kv"], a["kvs"], a["kr"], a["krs"], a["pos"], a["table"],
+                                      a["cache"], a["kvsc"], a["skipped"], a["B"], a["NB"], a["BS"],
+                                      a["M"], a["stream"])
+
+
+def test_append_fp8_rejects_bad_arguments_on_host(L):
+    assert _append8(B=0) == _lib.MLA_OK
+    for bad in (0.0, float("nan"), float("inf"), -float("inf")):
+        assert _append8(kvsc=bad) == _lib.MLA_ERR_BAD_SCALE, bad
+    assert _append8(kv=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append8(cache=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _append8(B=-1) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append8(kvs=500) == _lib.MLA_ERR_BAD_SHAPE
+    assert _append8(BS=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert _append8(BS=8) == _lib.MLA_ERR_UNSUPPORTED
+    assert _append8(cache=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    assert _append8(kv=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    assert _append8(pos=FAKE + 2) == _lib.MLA_ERR_ALIGNMENT
