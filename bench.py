@@ -206,8 +206,26 @@ def append_record(w, reps: int = 200, prewarm_ms: float = 0.0) -> dict:
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) / reps * 1e-3
     moved = w.B * 576 * 2 * 2  # each row read once and written once
+    # the fp8 form into an fp8 cache of the same shape (bf16 row read, e4m3 row written)
+    c8 = torch.empty(w.cache.shape, dtype=torch.uint8, device=dev)
+    kvs = 0.0625
+
+    def app8(i=0):
+        mla.append_latent_fp8(new[:, :512], new[:, 512:], pos, w.block_table, c8, kvs)
+    app8()
+    prewarm(app8, prewarm_ms)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        app8()
+    e1.record()
+    torch.cuda.synchronize()
+    t8 = e0.elapsed_time(e1) / reps * 1e-3
+    del c8
     return {"kernel": "mla_append_kernel", "rows": w.B, "launch_us": t * 1e6,
-            "gb_s": moved / t / 1e9}
+            "gb_s": moved / t / 1e9,
+            "fp8": {"kernel": "mla_append_fp8_kernel", "launch_us": t8 * 1e6,
+                    "gb_s": w.B * 576 * 3 / t8 / 1e9}}
 
 
 def absorb_record(B: int, H: int, reps: int = 100, prewarm_ms: float = 0.0) -> dict:
