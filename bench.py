@@ -134,12 +134,57 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
-    """Peaks this box attains with plain library kernels, timed with events: a
-    device-to-device copy of 2 GiB (reads and writes counted) and a bf16 GEMM
-    (8192^3 on hipBLASLt).  The attend kernel's rates are also given as
-    fractions of them."""
+def stream_read_record(gib: int = 4, reps: int = 5) -> dict:
+    """Read-only streaming bandwidth this GPU attains: the probe library's
+    plain 16-byte global loads (mode 0) and direct-to-LDS loads (mode 1, the
+    path the decode kernel stages rows with) over a 4 GiB buffer, 16x the
+    Infinity Cache, with 1, 2 and 4 workgroups of 256 threads per CU; HIP
+    events around `reps` launches of each.  Reports every setting and the best
+    per mode, in decimal GB/s."""
+    import ctypes
     import torch
+    from mla_latent_cache_absorbed_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.mla_probe_stream_read.restype = ctypes.c_size_t
+    lib.mla_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_probe_sink_bytes.restype = ctypes.c_size_t
+    lib.mla_probe_sink_bytes.argtypes = [ctypes.c_int32]
+    dev = torch.device("cuda")
+    x = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(lib.mla_probe_sink_bytes(4), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    runs = {}
+    for mode, name in ((0, "global_load_to_registers"), (1, "direct_to_lds")):
+        for wpc in (1, 2, 4):
+            n = lib.mla_probe_stream_read(x.data_ptr(), x.numel(), mode, wpc, sink.data_ptr(),
+                                          st.cuda_stream)
+            if n == 0:
+                raise RuntimeError("stream-read probe failed to launch")
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            for _ in range(reps):
+                lib.mla_probe_stream_read(x.data_ptr(), x.numel(), mode, wpc, sink.data_ptr(),
+                                          st.cuda_stream)
+            e1.record(st)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps * 1e-3
+            runs[f"{name}_wg{wpc}"] = n / t / 1e9
+    del x, sink
+    best = {m: max(v for k, v in runs.items() if k.startswith(m))
+            for m in ("global_load_to_registers", "direct_to_lds")}
+    return {"bytes_per_launch": int(n), "gb_s": runs, "best_gb_s": best,
+            "frac_of_peak": {m: v / HBM_PEAK_GBS for m, v in best.items()}}
+
+
+def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
+    """Peaks this box attains, timed with events: the read-only streaming
+    probes (see stream_read_record), a device-to-device copy of 2 GiB (reads
+    and writes counted) and a bf16 GEMM (8192^3 on hipBLASLt).  The attend
+    kernel's rates are also given as fractions of them."""
+    import torch
+    sr = stream_read_record()
     dev = torch.device("cuda")
     x = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
@@ -163,7 +208,9 @@ def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
     cp_gbs = 2 * x.numel() / t_cp / 1e9
     mm_tfs = 2 * 8192 ** 3 / t_mm / 1e12
     del x, y, a, bm
-    return {"copy_read_write_gbs": cp_gbs, "bf16_gemm_tflops": mm_tfs,
+    read_best = max(sr["best_gb_s"].values())
+    return {"stream_read": sr, "copy_read_write_gbs": cp_gbs, "bf16_gemm_tflops": mm_tfs,
+            "attend_frac_of_stream_read": achieved_gbs / read_best,
             "attend_frac_of_copy": achieved_gbs / cp_gbs,
             "attend_frac_of_gemm": tflops / mm_tfs}
 

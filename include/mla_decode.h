@@ -64,7 +64,9 @@ typedef enum {
   MLA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
   MLA_ERR_BAD_SHAPE = 2,    /* negative or overflowing sizes                      */
   MLA_ERR_UNSUPPORTED = 3,  /* H, BS or chunk_tokens outside the supported set    */
-  MLA_ERR_BAD_SCALE = 4,    /* scale is not finite                                */
+  MLA_ERR_BAD_SCALE = 4,    /* scale (or kv_scale) is not finite, or the factor the
+                               kernels apply to raw scores, scale * kv_scale * log2(e)
+                               rounded to fp32, overflows                         */
   MLA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required         */
   MLA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed         */
   MLA_ERR_ALIGNMENT = 7     /* a pointer violates the alignment stated above      */
@@ -155,8 +157,8 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
  *
  * (e4m3 values are exact in bf16, so products are exact and accumulate in
  * fp32 as for a bf16 cache.)  Supported: the head counts and block sizes of
- * mla_decode (otherwise MLA_ERR_UNSUPPORTED); kv_scale finite (else
- * MLA_ERR_BAD_SCALE).
+ * mla_decode (otherwise MLA_ERR_UNSUPPORTED); kv_scale finite and
+ * scale * kv_scale * log2(e) finite in fp32 (else MLA_ERR_BAD_SCALE).
  * Everything else (plan, workspace, layouts of q, block_table, seq_lens,
  * out, lse, errors) is as for mla_decode / mla_decode_attend; the plan call
  * is shared. */

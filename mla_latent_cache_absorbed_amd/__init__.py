@@ -28,23 +28,67 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _check_inputs(q, cache, table, lens):
-    if not (q.is_cuda and cache.is_cuda and table.is_cuda and lens.is_cuda):
-        raise ValueError("all inputs must be GPU tensors")
-    if q.dtype != torch.bfloat16 or cache.dtype != torch.bfloat16:
-        raise TypeError("q and latent_cache must be bfloat16")
-    if table.dtype != torch.int32 or lens.dtype != torch.int32:
-        raise TypeError("block_table and seq_lens must be int32")
-    if q.dim() != 3 or q.shape[2] != 576:
+def _tensor(name, t, dtype, shape=None, ndim=None):
+    """dtype, shape and contiguity of one argument (no device access)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _one_gpu(**named):
+    """Every tensor lives on the same GPU; returns that device.  Checked after
+    the dtype and shape checks, so that a host pointer never reaches a kernel."""
+    dev = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _check_outputs(out, lse, B, H):
+    _tensor("out", out, torch.bfloat16, (B, H, 512))
+    _tensor("lse", lse, torch.float32, (B, H))
+
+
+def _check_workspace(ws, B, H, M, BS, dev):
+    if not isinstance(ws, Workspace):
+        raise TypeError("workspace must be a Workspace")
+    if ws.shape != (B, H, M, BS):
+        raise ValueError(f"workspace was sized for (B, H, M, BS) = {ws.shape}, the call has "
+                         f"{(B, H, M, BS)}")
+    if ws.buf.device != dev:
+        raise ValueError(f"workspace is on {ws.buf.device}, the tensors on {dev}")
+
+
+def _check_inputs(q, cache, table, lens, cache_dtype=torch.bfloat16):
+    """Shapes and dtypes of the decode inputs; returns B, H, NB, BS, M."""
+    _tensor("q", q, torch.bfloat16, ndim=3)
+    if q.shape[2] != 576:
         raise ValueError(f"q must be [B, H, 576], got {tuple(q.shape)}")
-    if cache.dim() != 3 or cache.shape[2] != 576:
-        raise ValueError(f"latent_cache must be [NB, BS, 576], got {tuple(cache.shape)}")
-    B = q.shape[0]
-    if table.dim() != 2 or table.shape[0] != B or lens.shape != (B,):
-        raise ValueError("block_table must be [B, M] and seq_lens [B]")
-    for t in (q, cache, table, lens):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    cname = "latent_cache" if cache_dtype == torch.bfloat16 else "latent_cache_fp8"
+    _tensor(cname, cache, cache_dtype, ndim=3)
+    if cache.shape[2] != 576:
+        raise ValueError(f"{cname} must be [NB, BS, 576], got {tuple(cache.shape)}")
+    B, H = q.shape[0], q.shape[1]
+    _tensor("block_table", table, torch.int32, ndim=2)
+    if table.shape[0] != B:
+        raise ValueError(f"block_table must be [B, M] with B = {B}, got {tuple(table.shape)}")
+    if lens is not None:
+        _tensor("seq_lens", lens, torch.int32, (B,))
+    return B, H, cache.shape[0], cache.shape[1], table.shape[1]
 
 
 class Workspace:
@@ -82,37 +126,23 @@ def decode(q: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tenso
            lse: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None
            ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Absorbed MLA decode of one layer (plan + attend)."""
-    _check_inputs(q, latent_cache, block_table, seq_lens)
-    B, H, _ = q.shape
-    NB, BS, _ = latent_cache.shape
-    M = block_table.shape[1]
+    B, H, NB, BS, M = _check_inputs(q, latent_cache, block_table, seq_lens)
+    if out is not None or lse is not None:
+        if out is None or lse is None:
+            raise ValueError("pass both out and lse, or neither")
+        _check_outputs(out, lse, B, H)
+    dev = _one_gpu(q=q, latent_cache=latent_cache, block_table=block_table, seq_lens=seq_lens,
+                   out=out, lse=lse)
     if out is None:
-        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    ws = _ws(workspace, B, H, M, BS, q.device)
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = _ws(workspace, B, H, M, BS, dev)
+    _check_workspace(ws, B, H, M, BS, dev)
     st = _lib.mla_decode(q.data_ptr(), latent_cache.data_ptr(), block_table.data_ptr(),
                          seq_lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
                          B, H, NB, BS, M, ws.ptr, ws.nbytes, _stream())
     _lib._check("mla_decode", st)
     return out, lse
-
-
-def _check_fp8_inputs(q, cache8, table, lens):
-    if cache8.dtype != torch.uint8 or cache8.dim() != 3 or cache8.shape[2] != 576:
-        raise TypeError("latent_cache_fp8 must be a uint8 [NB, BS, 576] tensor of e4m3 bytes")
-    if not (q.is_cuda and cache8.is_cuda and table.is_cuda and lens.is_cuda):
-        raise ValueError("all inputs must be GPU tensors")
-    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 576:
-        raise ValueError("q must be bfloat16 [B, H, 576]")
-    if table.dtype != torch.int32 or lens.dtype != torch.int32:
-        raise TypeError("block_table and seq_lens must be int32")
-    B = q.shape[0]
-    if table.dim() != 2 or table.shape[0] != B or lens.shape != (B,):
-        raise ValueError("block_table must be [B, M] and seq_lens [B]")
-    for t in (q, cache8, table, lens):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
 
 
 def decode_fp8(q: torch.Tensor, latent_cache_fp8: torch.Tensor, block_table: torch.Tensor,
@@ -121,15 +151,18 @@ def decode_fp8(q: torch.Tensor, latent_cache_fp8: torch.Tensor, block_table: tor
                workspace: Optional[Workspace] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Absorbed MLA decode over an FP8 (e4m3) latent cache whose values are
     kv_scale * e4m3(byte); the same head counts and block sizes as decode()."""
-    _check_fp8_inputs(q, latent_cache_fp8, block_table, seq_lens)
-    B, H, _ = q.shape
-    NB, BS, _ = latent_cache_fp8.shape
-    M = block_table.shape[1]
+    B, H, NB, BS, M = _check_inputs(q, latent_cache_fp8, block_table, seq_lens, torch.uint8)
+    if out is not None or lse is not None:
+        if out is None or lse is None:
+            raise ValueError("pass both out and lse, or neither")
+        _check_outputs(out, lse, B, H)
+    dev = _one_gpu(q=q, latent_cache_fp8=latent_cache_fp8, block_table=block_table,
+                   seq_lens=seq_lens, out=out, lse=lse)
     if out is None:
-        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    ws = _ws(workspace, B, H, M, BS, q.device)
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    ws = _ws(workspace, B, H, M, BS, dev)
+    _check_workspace(ws, B, H, M, BS, dev)
     st = _lib.mla_decode_fp8(q.data_ptr(), latent_cache_fp8.data_ptr(), block_table.data_ptr(),
                              seq_lens.data_ptr(), float(scale), float(kv_scale), out.data_ptr(),
                              lse.data_ptr(), B, H, NB, BS, M, ws.ptr, ws.nbytes, _stream())
@@ -139,9 +172,12 @@ def decode_fp8(q: torch.Tensor, latent_cache_fp8: torch.Tensor, block_table: tor
 
 def attend_fp8(q, latent_cache_fp8, block_table, scale, kv_scale, out, lse,
                workspace: Workspace) -> None:
-    B, H, _ = q.shape
-    NB, BS, _ = latent_cache_fp8.shape
-    M = block_table.shape[1]
+    """The attend step over an FP8 cache, on a plan already in workspace."""
+    B, H, NB, BS, M = _check_inputs(q, latent_cache_fp8, block_table, None, torch.uint8)
+    _check_outputs(out, lse, B, H)
+    dev = _one_gpu(q=q, latent_cache_fp8=latent_cache_fp8, block_table=block_table, out=out,
+                   lse=lse)
+    _check_workspace(workspace, B, H, M, BS, dev)
     st = _lib.mla_decode_attend_fp8(q.data_ptr(), latent_cache_fp8.data_ptr(), block_table.data_ptr(),
                                     float(scale), float(kv_scale), out.data_ptr(), lse.data_ptr(),
                                     B, H, NB, BS, M, workspace.ptr, workspace.nbytes, _stream())
@@ -150,16 +186,22 @@ def attend_fp8(q, latent_cache_fp8, block_table, scale, kv_scale, out, lse,
 
 def plan(seq_lens: torch.Tensor, H: int, M: int, BS: int, workspace: Workspace,
          chunk_tokens: int = 0) -> None:
+    """The split-KV plan of one decode step into workspace (device-side, no sync)."""
+    _tensor("seq_lens", seq_lens, torch.int32, ndim=1)
     B = seq_lens.shape[0]
+    dev = _one_gpu(seq_lens=seq_lens)
+    _check_workspace(workspace, B, H, M, BS, dev)
     st = _lib.mla_decode_plan(seq_lens.data_ptr(), B, H, M, BS, chunk_tokens,
                               workspace.ptr, workspace.nbytes, _stream())
     _lib._check("mla_decode_plan", st)
 
 
 def attend(q, latent_cache, block_table, scale, out, lse, workspace: Workspace) -> None:
-    B, H, _ = q.shape
-    NB, BS, _ = latent_cache.shape
-    M = block_table.shape[1]
+    """The attend step (bf16 cache), on a plan already in workspace."""
+    B, H, NB, BS, M = _check_inputs(q, latent_cache, block_table, None)
+    _check_outputs(out, lse, B, H)
+    dev = _one_gpu(q=q, latent_cache=latent_cache, block_table=block_table, out=out, lse=lse)
+    _check_workspace(workspace, B, H, M, BS, dev)
     st = _lib.mla_decode_attend(q.data_ptr(), latent_cache.data_ptr(), block_table.data_ptr(),
                                 float(scale), out.data_ptr(), lse.data_ptr(), B, H, NB, BS, M,
                                 workspace.ptr, workspace.nbytes, _stream())
@@ -173,6 +215,8 @@ def _check_append_args(kv_c, k_rope, positions, block_table, cache, cache_dtype,
         raise ValueError(f"the cache must be {cache_dtype} [NB, BS, 576]")
     if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
         raise TypeError("positions and block_table must be int32")
+    if positions.dim() != 1:
+        raise ValueError(f"positions must be [B], got {tuple(positions.shape)}")
     B = positions.shape[0]
     if kv_c.dim() != 2 or k_rope.dim() != 2 or kv_c.shape[0] != B or k_rope.shape[0] != B:
         raise ValueError("kv_c and k_rope must be [B, n] with B = len(positions)")
@@ -182,8 +226,11 @@ def _check_append_args(kv_c, k_rope, positions, block_table, cache, cache_dtype,
         raise ValueError("block_table must be a contiguous [B, M] tensor")
     if not (cache.is_contiguous() and positions.is_contiguous()):
         raise ValueError("the cache and positions must be contiguous")
-    if skipped is not None and (skipped.dtype != torch.int32 or skipped.numel() < 1):
+    if skipped is not None and (not isinstance(skipped, torch.Tensor) or skipped.dtype != torch.int32
+                                or skipped.numel() < 1):
         raise TypeError("skipped must be an int32 device tensor")
+    _one_gpu(kv_c=kv_c, k_rope=k_rope, positions=positions, block_table=block_table, cache=cache,
+             skipped=skipped)
 
 
 def append_latent(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch.Tensor,
@@ -224,10 +271,9 @@ def append_latent_fp8(kv_c: torch.Tensor, k_rope: torch.Tensor, positions: torch
 
 
 def _bf16_contig(name, t, shape):
-    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
-        raise TypeError(f"{name} must be a contiguous bfloat16 GPU tensor")
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _tensor(name, t, torch.bfloat16, shape)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
 
 
 def absorb_prepare(w_uk: torch.Tensor) -> torch.Tensor:

@@ -10,6 +10,9 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "mla_decode.hip")
 SOURCES = [SRC, os.path.join(HERE, "csrc", "mla_append.hip"), os.path.join(HERE, "csrc", "mla_absorb.hip")]
 LIB = os.path.join(HERE, "libmla_decode.so")
+# read-bandwidth probes for the benchmark (not part of the decode path)
+PROBE_SRC = os.path.join(HERE, "csrc", "hbm_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,10 +28,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile ``libmla_decode.so``; returns its path.  Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+def _compile(sources, lib, verbose, extra=()):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,7 +40,14 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile ``libmla_decode.so`` (and the benchmark's ``libmla_probe.so``);
+    returns the decode library's path.  Always recompiles."""
+    _compile(SOURCES, LIB, verbose, extra)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     # MFMAs issued from inline asm: the compiler cannot see their operand
     # hazards, so the compiled code is checked for them
     from mla_latent_cache_absorbed_amd import isa_check

@@ -1,0 +1,99 @@
+// Read-only streaming probes of HBM bandwidth on gfx950, used by the
+// benchmark to state the read bandwidth this GPU attains next to its 8 TB/s
+// peak.  Not part of the decode path: built as its own small library.
+//
+//   mode 0  plain 16-byte global loads into registers, eight in flight per
+//           lane, folded with xor into one word per lane (written once);
+//   mode 1  16-byte direct-to-LDS loads, the path the decode kernel stages
+//           latent rows with: each wave keeps eight 1 KB loads in flight into
+//           its own 8 KB of LDS.
+//
+// Every workgroup walks the buffer with a grid stride, so consecutive
+// workgroups read consecutive 4 KB pieces.  bytes must be a multiple of
+// (grid * 32 KB); the host entry point rounds it down.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+constexpr size_t kStep = size_t(kThreads) * 16 * kUnroll;  // bytes per workgroup iteration
+
+__global__ __launch_bounds__(kThreads) void read_regs(const uint4* __restrict__ p, size_t n_iter,
+                                                      uint32_t* __restrict__ sink) {
+  const size_t grid = gridDim.x;
+  uint32_t acc = 0;
+  for (size_t it = 0; it < n_iter; ++it) {
+    const uint4* base = p + (it * grid + blockIdx.x) * (kStep / 16) + threadIdx.x;
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) v[j] = base[j * kThreads];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void read_lds(const char* __restrict__ p, size_t n_iter,
+                                                     uint32_t* __restrict__ sink) {
+  // 4 waves x 8 KB
+  __shared__ __attribute__((aligned(1024))) uint32_t ring[kThreads / 64 * 8 * 256];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t grid = gridDim.x;
+  uint32_t* mine = ring + w * 8 * 256;
+  for (size_t it = 0; it < n_iter; ++it) {
+    // the workgroup's 32 KB: wave w takes 1 KB pieces w, w + 4, ...
+    const char* base = p + (it * grid + blockIdx.x) * kStep + size_t(w) * 1024 + lane * 16;
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j)
+      __builtin_amdgcn_global_load_lds(base + j * 4096, mine + j * 256, 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's eight loads have landed
+  }
+  __syncthreads();
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) acc ^= mine[j * 256 + lane * 4];
+  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Streams `bytes` (rounded down to a whole number of workgroup iterations)
+// of the device buffer `buf` once, with `wg_per_cu` workgroups of 256
+// threads per compute unit, on `stream`.  `sink` is a device buffer of at
+// least mla_probe_sink_bytes(wg_per_cu) bytes.  Returns the bytes streamed,
+// or 0 on a bad argument or launch failure.
+size_t mla_probe_sink_bytes(int32_t wg_per_cu) {
+  int dev = 0, ncu = 0;
+  if (wg_per_cu < 1 || hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return size_t(ncu) * wg_per_cu * kThreads * 4;
+}
+
+size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_t wg_per_cu,
+                             void* sink, void* stream) {
+  if (!buf || !sink || wg_per_cu < 1 || (mode != 0 && mode != 1)) return 0;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const size_t grid = size_t(ncu) * wg_per_cu;
+  const size_t n_iter = bytes / (grid * kStep);
+  if (n_iter == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (mode == 0)
+    hipLaunchKernelGGL(read_regs, dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<const uint4*>(buf), n_iter, static_cast<uint32_t*>(sink));
+  else
+    hipLaunchKernelGGL(read_lds, dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<const char*>(buf), n_iter, static_cast<uint32_t*>(sink));
+  if (hipGetLastError() != hipSuccess) return 0;
+  return n_iter * grid * kStep;
+}
+
+}  // extern "C"

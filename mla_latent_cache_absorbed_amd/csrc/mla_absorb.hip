@@ -16,12 +16,16 @@
 // Both are per-head products with a small batch, Y[b,h,n] = sum_k
 // W[h,n,k] X[b,h,k], and one kernel serves both: each wave computes 32x32
 // tiles of Y^T (32 rows n of W against 32 requests b) over the whole K on
-// 32x32x16 bf16 MFMA, loading both operands straight from global memory as
-// 16-byte K-contiguous fragments.  W_UK is used transposed ([H, 512, 128], K
-// contiguous); mla_absorb_prepare makes that copy once, when the weights are
-// loaded.  The four waves of a workgroup share the W rows (their four request
-// tiles); all workgroups of one head land on one XCD, so the head's X rows are
-// read from HBM once and then from that XCD's L2.
+// 32x32x16 bf16 MFMA.  The K dimension goes in chunks of 128: each chunk's W
+// rows and X rows are staged in LDS with coalesced 16-byte loads (16-byte
+// chunk c of row r at slot c ^ (r % 16)), the MFMA fragments are read from
+// there, and the output tile goes back through LDS so that each request's
+// contiguous output bytes are stored by consecutive lanes.  W_UK is used
+// transposed ([H, 512, 128], K contiguous); mla_absorb_prepare makes that
+// copy once, when the weights are loaded.  The four waves of a workgroup
+// share the W rows (their four request tiles); all workgroups of one head
+// land on one XCD, so the head's X rows are read from HBM once and then from
+// that XCD's L2.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

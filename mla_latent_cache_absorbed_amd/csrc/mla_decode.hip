@@ -2137,6 +2137,12 @@ hipError_t launch_attend(const AttendArgs& a, int grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The factor the kernels apply to raw scores: scale * kv_scale * log2(e), in
+// fp32 as they receive it.  Finite inputs can still overflow it (scale near
+// the fp32 maximum, or a large product), which would turn every score into
+// +-inf and the outputs into NaN, so it is checked on its own.
+float scale_log2(float scale, float kv_scale) { return scale * kv_scale * 1.4426950408889634f; }
+
 mla_status validate_attend(const void* q, const void* latent_cache, const int32_t* block_table,
                            float scale, const void* out, const float* lse, int32_t B, int32_t H,
                            int32_t NB, int32_t BS, int32_t M, const void* workspace,
@@ -2149,7 +2155,7 @@ mla_status validate_attend(const void* q, const void* latent_cache, const int32_
   if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
       !aligned(block_table, 4))
     return MLA_ERR_ALIGNMENT;
-  if (!isfinite(scale)) return MLA_ERR_BAD_SCALE;
+  if (!isfinite(scale) || !isfinite(scale_log2(scale, 1.0f))) return MLA_ERR_BAD_SCALE;
   return check_workspace(workspace, workspace_bytes, B, H);
 }
 
@@ -2161,7 +2167,7 @@ mla_status validate_attend_fp8(const void* q, const void* latent_cache, const in
   mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
                                  workspace, workspace_bytes);
   if (s != MLA_OK) return s;
-  if (!isfinite(kv_scale)) return MLA_ERR_BAD_SCALE;
+  if (!isfinite(kv_scale) || !isfinite(scale_log2(scale, kv_scale))) return MLA_ERR_BAD_SCALE;
   return MLA_OK;
 }
 
@@ -2183,7 +2189,7 @@ AttendArgs attend_args(const void* q, const void* latent_cache, const int32_t* b
   a.big = reinterpret_cast<const int32_t*>(ws + L.big_off);
   a.part_lse = reinterpret_cast<float*>(ws + L.plse_off);
   a.part_o = reinterpret_cast<float*>(ws + L.po_off);
-  a.scale_log2 = scale * kv_scale * 1.4426950408889634f;
+  a.scale_log2 = scale_log2(scale, kv_scale);
   a.v_scale = kv_scale;
   a.B = B;
   a.H = H;

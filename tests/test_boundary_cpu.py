@@ -251,3 +251,25 @@ def test_append_fp8_rejects_bad_arguments_on_host(L):
     assert _append8(cache=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
     assert _append8(kv=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
     assert _append8(pos=FAKE + 2) == _lib.MLA_ERR_ALIGNMENT
+
+
+def test_overflowing_score_factor_is_rejected_on_host(L):
+    """scale and kv_scale are each finite, but the factor the kernels apply to
+    raw scores (scale * kv_scale * log2 e, in fp32) overflows: rejected with
+    MLA_ERR_BAD_SCALE before any launch, for both caches and both entry points."""
+    big = 3.0e38  # finite in fp32; times log2(e) it overflows
+    assert _decode(scale=big) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode(scale=-big) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode8(scale=1e30, kv=1e10) == _lib.MLA_ERR_BAD_SCALE
+    assert _decode8(scale=-1e30, kv=1e10) == _lib.MLA_ERR_BAD_SCALE
+    A = _lib.mla_decode_attend
+    assert A(FAKE, FAKE, FAKE, big, FAKE, FAKE, 2, 128, 14, 16, 7, FAKE, 1 << 40, None) \
+        == _lib.MLA_ERR_BAD_SCALE
+    A8 = _lib.mla_decode_attend_fp8
+    assert A8(FAKE, FAKE, FAKE, 1e30, 1e10, FAKE, FAKE, 2, 128, 14, 64, 7, FAKE, 1 << 40, None) \
+        == _lib.MLA_ERR_BAD_SCALE
+    # a large but representable factor is accepted by the host checks (it
+    # only reaches the launch, which fails without a device)
+    if _no_device():
+        assert _decode(scale=1e30) == _lib.MLA_ERR_HIP
+        assert _decode8(scale=1e20, kv=1e10) == _lib.MLA_ERR_HIP

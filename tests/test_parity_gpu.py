@@ -315,6 +315,77 @@ def test_full_size_sampled(name, reqs):
     _assert_parity(o[reqs], l[reqs], ro, rl, f"{name} requests {reqs}")
 
 
+def test_step61_sampled_layers():
+    """The full 61-layer decode step in the launch pattern the benchmark times:
+    61 separate caches (layer l draws its query and cache with seed l), one
+    plan for the step, then one attend per layer into its own out/lse, all on
+    one stream with no synchronisation in between.  Layers 0, 30 and 60 are
+    checked against the oracle on sampled requests; every layer's outputs must
+    be finite, and the plan's queues must be back at zero afterwards."""
+    spec = wl.spec("step61")
+    _say(f"[step61] generating {spec.layers} layers")
+    layers = [wl.make("step61", device="cuda", seed=0, layer=l) for l in range(spec.layers)]
+    w0 = layers[0]
+    for w in layers[1:]:  # one shared table and length vector, fresh data per layer
+        assert torch.equal(w.block_table, w0.block_table) and torch.equal(w.seq_lens, w0.seq_lens)
+    ws = mla.Workspace(w0.B, w0.H, w0.M, w0.BS)
+    outs = [torch.empty((w0.B, w0.H, 512), dtype=torch.bfloat16, device="cuda") for _ in layers]
+    lses = [torch.empty((w0.B, w0.H), dtype=torch.float32, device="cuda") for _ in layers]
+    torch.cuda.synchronize()
+    mla.plan(w0.seq_lens, w0.H, w0.M, w0.BS, ws)
+    for w, o, l in zip(layers, outs, lses):
+        mla.attend(w.q, w.cache, w.block_table, w.scale, o, l, ws)
+    torch.cuda.synchronize()
+    hdr = ws.header()
+    _say(f"[step61] plan items={hdr[0]} chunk={hdr[1]} flags={hdr[2]}")
+    assert hdr[2] == 0 and hdr[3] == 0 and hdr[6] == 0
+    assert ws.check_flags() == 0
+    for o, l in zip(outs, lses):
+        assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+    # distinct layers give distinct outputs (each attend read its own cache)
+    assert not torch.equal(outs[0], outs[1])
+    reqs = [0, 61, 123]
+    for li in (0, 30, 60):
+        w = layers[li]
+        ro, rl = _sampled_oracle(w, reqs)
+        _assert_parity(outs[li].float().cpu().numpy()[reqs], lses[li].cpu().numpy()[reqs], ro, rl,
+                       f"step61 layer {li} requests {reqs}")
+    del layers, outs, lses
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("H", [128, 16])
+def test_contract_violations_are_flagged_and_contained(H):
+    """One batch with an over-long length, a negative length and a request
+    whose used block-table entry is out of range, next to normal requests:
+    both data-check bits are raised, the clamps keep every access in bounds
+    (the over-long request reads the poisoned spare block, so its own output
+    is unspecified), and the normal requests still match the oracle."""
+    lens = [300, 500, 200, 700, 150]
+    w = wl.make_custom(lens, H=H, BS=64, seed=53, poison_unused=True)
+    M = w.M
+    seq = w.seq_lens.clone()
+    seq[1] = M * w.BS + 1000     # longer than the table can hold: clamped to M * BS
+    seq[3] = -5                  # negative: clamped to 0
+    table = w.block_table.clone()
+    table[2, 1] = w.NB + 7       # a used entry (tokens 64..127) past the cache
+    w = _to_gpu(wl.Workload(w.name, w.q, w.cache, table, seq, w.scale))
+    ws = mla.Workspace(w.B, w.H, w.M, w.BS, w.q.device)
+    for chunk in (None, 128):
+        out, lse = _run(w, chunk_tokens=chunk, ws=ws)
+        flags = ws.check_flags()
+        _say(f"[violations] H={H} chunk={chunk}: flags {flags}")
+        assert flags & mla._lib.MLA_CHECK_SEQ_LEN_RANGE
+        assert flags & mla._lib.MLA_CHECK_BLOCK_ID_RANGE
+        assert not flags & mla._lib.MLA_CHECK_MERGE_WAIT
+        normal = [0, 4]
+        ref = wl.make_custom(lens, H=H, BS=64, seed=53, poison_unused=True)
+        ro, rl = _oracle(ref, requests=normal)
+        _assert_parity(out[normal], lse[normal], ro, rl, f"normal requests beside violations H={H}")
+        # the negative length is clamped to an empty request
+        assert np.all(out[3] == 0) and np.all(np.isneginf(lse[3]))
+
+
 @pytest.mark.parametrize("H", [128, 16])
 @pytest.mark.parametrize("scale", [0.0, -0.072, 0.5])
 def test_degenerate_and_negative_scales(H, scale):
