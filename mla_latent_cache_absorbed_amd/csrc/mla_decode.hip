@@ -49,6 +49,7 @@ constexpr int kHdrBytes = 256;
 constexpr float kRefHeadroom = 64.0f;     // log2 units: P <= 2^64 before an item is redone
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kSc1 = 16;                  // cache-policy bit sc1: agent-scope coherent access
+constexpr int kSc0 = 1;                   // cache-policy bit sc0: misses L1
 constexpr int kMergeMinItems = 3;         // splits this wide are merged by merge units
 // Per-request counters: tickets taken (or merge units done) and partials
 // published.  Both are 0 between calls.
@@ -151,6 +152,18 @@ __device__ __forceinline__ int lane0_fetch_add(int32_t* p, int v) {
       : "memory");
   return res;
 }
+// Lane 0 adds v to *p (relaxed, agent scope), without waiting for it.
+__device__ __forceinline__ void lane0_atomic_add(int32_t* p, int v) {
+  uint64_t keep;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %1, %2, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(keep)
+      : "v"(p), "v"(v)
+      : "memory");
+}
 // Lane 0 ors v into *p (relaxed, agent scope).
 __device__ __forceinline__ void lane0_atomic_or(int32_t* p, int v) {
   uint64_t keep;
@@ -176,6 +189,30 @@ __device__ __forceinline__ void wave_poll(int32_t* p, int target, int32_t* flags
     }
     __builtin_amdgcn_s_sleep(2);
   }
+}
+
+// As wave_poll, for a word that a partner sets to a non-zero value; returns
+// the value seen (0 if the bound was hit).
+__device__ __forceinline__ int wave_poll_value(int32_t* p, int32_t* flags, int flag) {
+  for (int spin = 0;; ++spin) {
+    const int v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v != 0) return v;
+    if (spin >= (1 << 22)) {
+      lane0_atomic_or(flags, flag);
+      return 0;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The XCD (accelerator complex die) this wave runs on.  Each XCD has its own
+// L2; a buffer written through to memory by one wave is read back coherently
+// by a wave of the same XCD with a load that only misses L1.
+__device__ __forceinline__ int xcd_id() {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+  return x;
 }
 
 // MFMAs of the hot loop are written out so that register classes are pinned:
@@ -256,6 +293,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* cache, 
 // states, for a buffer resource or M0 just written by a VALU instruction
 // (the compiler reloads spilled SGPRs with v_readlane), which also covers the
 // one needed after an SALU write of M0.
+__device__ __forceinline__ void dma16_buffer_sc0(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 const char LDS_AS* dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)dst;
+  // sc0: misses L1, may hit the L2 of this XCD
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen sc0 lds"
+               :: "v"(voff), "s"(r), "{m0}"(m0));
+}
 __device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                              const char LDS_AS* dst) {
   const uint32_t m0 = (uint32_t)(uintptr_t)dst;
@@ -586,6 +630,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
   // fetch of all (it returns n_items - 1) leaves the queue at 0 so that the
   // same plan serves the next call.
   const int grid = int(gridDim.x);
+  const int xcd = xcd_id();
   bool first = true;
   for (;;) {
     int it = int(blockIdx.x);
@@ -1063,112 +1108,145 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       publish();
       continue;
     }
-    // Two items: the item takes its ticket first; the first publishes and
-    // waits no further, the last waits until its partner has published and
-    // merges.
-    if (w == 0) {
-      const int t = lane0_fetch_add(&a.ctr[kCtr * b + kTicket], 1);
-      *s_ticket = t;
-    }
-    __syncthreads();
-    const int ticket = __builtin_amdgcn_readfirstlane(*s_ticket);
-    if (ticket == 0) {
-      publish();
-      continue;
-    }
-    // The partner took its ticket earlier, so it is past its stage loop and
-    // only has stores left; the wait ends.  It is bounded all the same, and
-    // a flag is raised if the bound is hit.
-    if (w == 0) {
-      wave_poll(&a.ctr[kCtr * b + kPublished], 1, &a.hdr[2], MLA_CHECK_MERGE_WAIT);
-      // leave the counters ready for the next call
-      __hip_atomic_store(&a.ctr[kCtr * b + kTicket], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctr[kCtr * b + kPublished], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    {
-      // log-sum-exp merge (log2 domain): lse = log2 sum_s 2^lse_s,
-      // out = sum_s 2^(lse_s - lse) o_s, with o_s the normalised partials.
-      // Terms are summed in item order, and this item's own term is the very
-      // value it would have published, so the result does not depend on
-      // which item finished last.
+    // Two items: a symmetric half merge.  Item s of the request (s = 0 for
+    // the item over the first tokens) merges head blocks [s NW/2, (s+1)
+    // NW/2) and publishes the other half for its partner, so each item
+    // stores and loads half a partial and both halves of the output are
+    // written at once; no item waits for a ticket.  The request's two
+    // counters become one publish word per item: 0 until the item's half is
+    // out, then 1 + the XCD it ran on.  Halves are written through to memory
+    // (sc1), so every reader sees them; a reader on the publisher's XCD
+    // loads them with L1-missing loads that the shared L2 can serve, any
+    // other reader with agent-scope loads.  Each item clears its partner's
+    // word once it has read the half, which leaves both at zero for the next
+    // call.
+    auto half_merge = [&](auto me_c) {
+      constexpr int me = decltype(me_c)::value;
+      constexpr int kHalf = NW / 2;              // head blocks per half
+      constexpr int mine0 = me * kHalf;          // first head block this item merges
+      constexpr int theirs0 = (1 - me) * kHalf;  // first head block it publishes
       const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
-      auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
-      const int s0 = slot_of(0), s1 = slot_of(1);
-      const bool own_first = s0 == it;
-      const int other = own_first ? s1 : s0;
-      const __amdgpu_buffer_rsrc_t pr = part_rsrc(other);
-      // The partner's blocks of this wave's slab come in through this wave's
-      // 36 KB of the LDS ring, free now, with direct-to-LDS loads in rounds
-      // of up to 36: every load of a round is in flight at once, and the
-      // blocks land in LDS in the layout they were stored in.  The
-      // log-sum-exps load meanwhile.
-      // (fp8: the ring's share of a wave, whole KB, at most 36 KB)
+      const int other = me ? ((0 < rq[1]) ? rq[0] : rq[2]) : ((1 < rq[1]) ? rq[0] + 1 : rq[2]);
+      {
+        const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
+#pragma unroll
+        for (int hh = 0; hh < kHalf; ++hh)
+#pragma unroll
+          for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int h = theirs0 + hh;
+              f32x4 v4;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v4[r] = o[h * CPW + c][4 * g + r] * inv[h];
+              __builtin_amdgcn_raw_buffer_store_b128(v4, pr, slab + pad[h] + (64 * h + 4 * c + g) * 1024, 0, kSc1);
+            }
+        // every lane stores its head's log-sum-exp (the partner reads those of its half)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's half is out
+        __syncthreads();
+        if (w == 0)
+          __hip_atomic_store(&a.ctr[kCtr * b + me], 1 + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // The partner is running (both items of a request are taken before
+      // either can finish), so the wait ends; it is bounded all the same.
+      if (w == 0) *s_item = wave_poll_value(&a.ctr[kCtr * b + (1 - me)], &a.hdr[2], MLA_CHECK_MERGE_WAIT);
+      __syncthreads();
+      const bool near = __builtin_amdgcn_readfirstlane(*s_item) == 1 + xcd;
+      // log-sum-exp merge (log2 domain): lse = log2 sum_s 2^lse_s,
+      // out = sum_s 2^(lse_s - lse) o_s, with o_s the normalised partials,
+      // summed in item order; this item's own term is the value it would
+      // have published, so the result does not depend on which item merges
+      // which half.  The partner's blocks of this wave's slab for this
+      // item's half come in through the wave's part of the (free) LDS ring.
       constexpr int kWB8 = kRing / NW / 1024 * 1024;
       constexpr int kWaveBuf = (kF8 && kWB8 < kStageBytes) ? kWB8 : kStageBytes;
       static_assert(NW * kWaveBuf <= kRing, "merge staging fits the ring");
+      constexpr int kBlocks = kHalf * CPW * 4;   // 1 KB blocks per wave
+      static_assert(kBlocks * 1024 <= kWaveBuf, "one round of loads");
       char LDS_AS* mb = lds + w * kWaveBuf;
-      constexpr int kRound = kWaveBuf / 1024;  // 36 blocks (fp8: up to 36)
-      constexpr int kBlocks = NW * CPW * 4;       // 64 blocks per wave
-      auto blk_off = [&](int j) {  // block j = (h, c, g) of this wave's slab
-        const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
-        return slab + pad[h] + uint32_t(64 * h + 4 * c + g) * 1024;
-      };
-      float wa[NW], wb[NW];  // weights of the first and the second item, per head block
-      float lse_out = 0.0f;
+      const __amdgpu_buffer_rsrc_t pr = part_rsrc(other);
+      asm volatile("" ::: "memory");
+      float lo[kHalf];
+      if (near) {
 #pragma unroll
-      for (int r0 = 0; r0 < kBlocks; r0 += kRound) {
-        const int n = (kBlocks - r0) < kRound ? (kBlocks - r0) : kRound;
-        asm volatile("" ::: "memory");  // the previous round's LDS reads stay above
-#pragma unroll
-        for (int j = 0; j < kRound; ++j)
-          if (j < n) dma16_buffer(pr, blk_off(r0 + j), mb + j * 1024);
-        if (r0 == 0) {
-          float lo[NW];
-#pragma unroll
-          for (int h = 0; h < NW; ++h)
-            lo[h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                plse_r, uint32_t(other * HP + h * 32 + hl_e) * 4, 0, kSc1));
-#pragma unroll
-          for (int h = 0; h < NW; ++h) {
-            const float lown = x_lse[h * 32 + hl_e];
-            const float l0 = own_first ? lown : lo[h], l1 = own_first ? lo[h] : lown;
-            const float mlse = fmaxf(l0, l1);
-            const float e0 = __builtin_amdgcn_exp2f(l0 - mlse), e1 = __builtin_amdgcn_exp2f(l1 - mlse);
-            const float lam = e0 + e1;
-            const float rl = 1.0f / lam;
-            wa[h] = e0 * rl;
-            wb[h] = e1 * rl;
-            if (h == w) lse_out = (mlse + log2f(lam)) * kLn2;
-          }
+        for (int j = 0; j < kBlocks; ++j) {
+          const int hh = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+          const int h = mine0 + hh;
+          dma16_buffer_sc0(pr, slab + pad[h] + uint32_t(64 * h + 4 * c + g) * 1024, mb + j * 1024);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // LDS reads are not moved above earlier buffer stores: read a group
-        // of blocks, then combine and store them.
-        constexpr int kGroup = 6;
 #pragma unroll
-        for (int jg = 0; jg < kRound; jg += kGroup) {
-          f32x4 xs[kGroup];
+        for (int hh = 0; hh < kHalf; ++hh)
+          lo[hh] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              plse_r, uint32_t(other * HP + (mine0 + hh) * 32 + hl_e) * 4, 0, kSc0));
+      } else {
 #pragma unroll
-          for (int jj = 0; jj < kGroup; ++jj)
-            if (jg + jj < n) xs[jj] = *(const f32x4 LDS_AS*)(mb + (jg + jj) * 1024 + lane_e * 16);
+        for (int j = 0; j < kBlocks; ++j) {
+          const int hh = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+          const int h = mine0 + hh;
+          dma16_buffer(pr, slab + pad[h] + uint32_t(64 * h + 4 * c + g) * 1024, mb + j * 1024);
+        }
 #pragma unroll
-          for (int jj = 0; jj < kGroup; ++jj) {
-            if (jg + jj < n) {
-              const int j = r0 + jg + jj;
-              const int h = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
-              float v[4];
+        for (int hh = 0; hh < kHalf; ++hh)
+          lo[hh] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              plse_r, uint32_t(other * HP + (mine0 + hh) * 32 + hl_e) * 4, 0, kSc1));
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // every wave has read its part of the partner's half: clear the
+      // partner's word for the next call
+      __syncthreads();
+      if (w == 0)
+        __hip_atomic_store(&a.ctr[kCtr * b + (1 - me)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      float wa[kHalf], wb[kHalf];  // weights of the first and the second item
+      float lse_out = 0.0f;
+      bool lse_mine = false;       // this wave's head block lies in this item's half
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float own = o[h * CPW + c][4 * g + r] * inv[h];
-                v[r] = own_first ? fmaf(wb[h], xs[jj][r], wa[h] * own) : fmaf(wb[h], own, wa[h] * xs[jj][r]);
-              }
-              store_out4(h, c, g, v);
-            }
-          }
+      for (int hh = 0; hh < kHalf; ++hh) {
+        const int h = mine0 + hh;
+        const float lown = x_lse[h * 32 + hl_e];
+        const float l0 = me ? lo[hh] : lown, l1 = me ? lown : lo[hh];
+        const float mlse = fmaxf(l0, l1);
+        const float e0 = __builtin_amdgcn_exp2f(l0 - mlse), e1 = __builtin_amdgcn_exp2f(l1 - mlse);
+        const float lam = e0 + e1;
+        const float rl = 1.0f / lam;
+        wa[hh] = e0 * rl;
+        wb[hh] = e1 * rl;
+        if (h == w) {
+          lse_out = (mlse + log2f(lam)) * kLn2;
+          lse_mine = true;
         }
       }
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_out), lse_r, head_e * 4, 0, 0);
+      constexpr int kGroup = 8;
+      static_assert(kBlocks % kGroup == 0, "groups of blocks");
+#pragma unroll
+      for (int jg = 0; jg < kBlocks; jg += kGroup) {
+        f32x4 xs[kGroup];
+#pragma unroll
+        for (int jj = 0; jj < kGroup; ++jj) xs[jj] = *(const f32x4 LDS_AS*)(mb + (jg + jj) * 1024 + lane_e * 16);
+#pragma unroll
+        for (int jj = 0; jj < kGroup; ++jj) {
+          const int j = jg + jj;
+          const int hh = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+          const int h = mine0 + hh;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float own = o[h * CPW + c][4 * g + r] * inv[h];
+            v[r] = me ? fmaf(wb[hh], own, wa[hh] * xs[jj][r]) : fmaf(wb[hh], xs[jj][r], wa[hh] * own);
+          }
+          store_out4(h, c, g, v);
+        }
+      }
+      // the lse of this wave's head block, if that block is in this item's
+      // half (stores of the other waves fall outside the resource)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_out), lse_r,
+                                            lse_mine ? uint32_t(head_e) * 4 : 0x40000000u, 0, 0);
+    };
+    {
+      const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
+      const int s0 = (0 < rq[1]) ? rq[0] : rq[2];
+      if (s0 == it) half_merge(BoolC<false>{});
+      else half_merge(BoolC<true>{});
     }
     __syncthreads();
   }
@@ -1884,6 +1962,7 @@ __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
   Scan4 r;
   r.incl = make_int4(x.x + pre.x, x.y + pre.y, x.z + pre.z, x.w + pre.w);
   r.total = tot;
+  __syncthreads();  // every wave has read s_scan before the next scan writes it
   return r;
 }
 
@@ -1892,7 +1971,7 @@ __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
 // the (clamped) lengths are read from memory once and kept in LDS.
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
-    int ovh, int cap, int units_per_req, int32_t* __restrict__ hdr, int4* __restrict__ req,
+    int ovh, int cap, int units_per_req, int nx, int32_t* __restrict__ hdr, int4* __restrict__ req,
     int32_t* __restrict__ ctr, int32_t* __restrict__ big, int4* __restrict__ items) {
   __shared__ long long s_cost[kPlanThreads / 64];
   __shared__ int s_chunk[kPlanThreads / 64];
@@ -2012,55 +2091,86 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     }
   }
 
-  // 2) totals: full chunks, remainders, empty requests, range-check bits;
-  //    the counters of every request start at 0
-  int4 loc = make_int4(0, 0, 0, bad);
+  // 2) totals: requests split into exactly two items (pairs), and the full
+  //    chunks, remainders and empty requests of all other requests; the
+  //    range-check bits; the counters of every request start at 0
+  int4 loc = make_int4(0, 0, 0, 0);
   for (int b = tid; b < B; b += kPlanThreads) {
     const int L = len_of(b);
-    loc.x += L / chunk;
-    loc.y += (L % chunk) ? 1 : 0;
+    const int nf = L / chunk, nr = (L % chunk) ? 1 : 0;
+    const bool pair = nf + nr == 2;
+    loc.x += pair ? 0 : nf;
+    loc.y += pair ? 0 : nr;
     loc.z += (L == 0) ? 1 : 0;
+    loc.w += pair ? 1 : 0;
 #pragma unroll
     for (int k = 0; k < kCtr; ++k) ctr[kCtr * b + k] = 0;
   }
   const int4 tot = block_scan4(loc, s_scan).total;
-  const int NF = tot.x, NR = tot.y, NE = tot.z, any_bad = tot.w;
+  const int NF = tot.x, NR = tot.y, NE = tot.z, NP = tot.w;
+  const int any_bad = __syncthreads_or(bad);
+  // Pairs come first.  The two items of pair j of the first nx * G pairs
+  // (G = NP / nx) sit nx positions apart, so that workgroups w and w + nx,
+  // which the dispatcher places on the same XCD, take them; the last
+  // NP % nx pairs follow side by side, then the other items in the order
+  // full chunks, remainders, empty requests.
+  const int G = NP / nx;
+  auto pair_pos = [&](int j, int half) {
+    if (j < G * nx) return 2 * nx * (j / nx) + (j % nx) + half * nx;
+    return 2 * j + half;
+  };
+  const int Q0 = 2 * NP;  // first position of the other items
 
   // 3) per-request placement from exclusive scans; requests split into
   //    kMergeMinItems or more items are listed for the merge units
   int4 carry = make_int4(0, 0, 0, 0);
+  int carry_big = 0;
   for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
     const int b = b0 + tid;
     const int L = (b < B) ? len_of(b) : 0;
-    const int nf = L / chunk;
-    const int nr = (L % chunk) ? 1 : 0;
+    const int nf0 = L / chunk;
+    const int nr0 = (L % chunk) ? 1 : 0;
+    const int cnt = nf0 + nr0;
+    const bool pair = b < B && cnt == 2;
+    const int nf = pair ? 0 : nf0, nr = pair ? 0 : nr0;
     const int ne = (b < B && L == 0) ? 1 : 0;
-    const int cnt = nf + nr;
+    const int np = pair ? 1 : 0;
     const int nbg = (b < B && cnt >= kMergeMinItems) ? 1 : 0;
-    const Scan4 sc = block_scan4(make_int4(nf, nr, ne, nbg), s_scan);
+    const Scan4 sc = block_scan4(make_int4(nf, nr, ne, np), s_scan);
+    const Scan4 sb = block_scan4(make_int4(nbg, 0, 0, 0), s_scan);
+    const int big_incl = sb.incl.x;
     if (b < B) {
-      const int fbeg = carry.x + sc.incl.x - nf;
-      const int ritem = nr ? (NF + carry.y + sc.incl.y - nr) : -1;
-      req[b] = make_int4(fbeg, nf, ritem, cnt);
-      for (int s = 0; s < nf; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
-      if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt);
-      if (ne) items[NF + NR + carry.z + sc.incl.z - 1] = make_int4(b, 0, 0, 0);
-      if (nbg) big[carry.w + sc.incl.w - 1] = b;
+      if (pair) {
+        const int j = carry.w + sc.incl.w - 1;
+        const int p0 = pair_pos(j, 0), p1 = pair_pos(j, 1);
+        req[b] = make_int4(p0, 1, p1, 2);
+        items[p0] = make_int4(b, 0, chunk, 2);
+        items[p1] = make_int4(b, chunk, L, 2);
+      } else {
+        const int fbeg = Q0 + carry.x + sc.incl.x - nf;
+        const int ritem = nr ? (Q0 + NF + carry.y + sc.incl.y - nr) : -1;
+        req[b] = make_int4(fbeg, nf, ritem, cnt);
+        for (int s = 0; s < nf; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
+        if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt);
+        if (ne) items[Q0 + NF + NR + carry.z + sc.incl.z - 1] = make_int4(b, 0, 0, 0);
+        if (nbg) big[carry_big + big_incl - 1] = b;
+      }
     }
     carry.x += sc.total.x;
     carry.y += sc.total.y;
     carry.z += sc.total.z;
     carry.w += sc.total.w;
+    carry_big += sb.total.x;
   }
 
   // 4) header
   if (tid == 0) {
-    hdr[0] = NF + NR + NE;
+    hdr[0] = 2 * NP + NF + NR + NE;
     hdr[1] = chunk;
     hdr[2] = any_bad ? MLA_CHECK_SEQ_LEN_RANGE : 0;
     hdr[3] = 0;
-    hdr[4] = NF;
-    hdr[5] = carry.w * units_per_req;
+    hdr[4] = 2 * nx * G;  // items placed as XCD-sharing pairs
+    hdr[5] = carry_big * units_per_req;
     hdr[6] = 0;
   }
 }
@@ -2080,6 +2190,22 @@ mla_status device_cu_count(int* n) {
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return MLA_ERR_HIP;
     g_cu_count[dev] = c;
+  }
+  *n = c;
+  return MLA_OK;
+}
+
+int g_xcd_count[kMaxDevices];  // 0 = not queried yet
+
+// XCDs of the current device (1 where the runtime does not report them).
+mla_status device_xcd_count(int* n) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  int c = g_xcd_count[dev];
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || c < 1) c = 1;
+    g_xcd_count[dev] = c;
   }
   *n = c;
   return MLA_OK;
@@ -2230,14 +2356,18 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_
                            size_t workspace_bytes, void* stream) {
   mla_status s = validate_plan(seq_lens, B, H, M, BS, chunk_tokens, workspace, workspace_bytes);
   if (s != MLA_OK || B == 0) return s;
-  int ncu = 0;
+  int ncu = 0, nxcd = 1;
   if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  if ((s = device_xcd_count(&nxcd)) != MLA_OK) return s;
   const WsLayout L = ws_layout(B, H);
   const Variant v = pick_variant(H);
+  // the wide kernels take their first items in workgroup order, so pairs
+  // placed nx apart land on one XCD; the narrow kernel's workers do not
+  const int nx = v.nw ? nxcd : 1;
   char* ws = static_cast<char*>(workspace);
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
                      seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.workers_per_cu,
-                     (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req,
+                     (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req, nx,
                      reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
                      reinterpret_cast<int32_t*>(ws + L.ctr_off),
                      reinterpret_cast<int32_t*>(ws + L.big_off),
