@@ -142,6 +142,30 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* The whole decode (plan + attend) without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, layouts,
+ * results and errors as mla_decode, except:
+ *   - the plan and split partials live in a library-owned device array of
+ *     64 MiB, one per GPU the library runs on, held until the process ends;
+ *     its device address is taken on the first call on each device;
+ *   - batches whose plan and partials do not fit it return MLA_ERR_WORKSPACE
+ *     before anything is enqueued (at 128 heads that is B above 255; the
+ *     plan is limited to the work items that fit, which for large splits can
+ *     give a coarser split than mla_decode chooses, never a different result
+ *     beyond rounding);
+ *   - every call on one GPU shares that array, so calls on one GPU must not
+ *     overlap: two such calls in flight at once (on different streams, or
+ *     from different host threads without ordering) race and their results
+ *     are unspecified.  Each call's plan rewrites every word the attend step
+ *     reads and leaves its counters at zero.
+ * It calls no hipMalloc, hipFree or other allocating routine. */
+mla_status mla_decode_noalloc(const void* q, const void* latent_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              float scale, void* out, float* lse,
+                              int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M,
+                              void* stream);
+
 /* FP8 latent cache.  The cache holds one byte per element, OCP e4m3 (sign,
  * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F and
  * 0xFF are NaN), 576 bytes per token: [NB, BS, 576], elements 0..511 kv_c

@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import MlaError  # noqa: F401
 
-__all__ = ["decode", "Workspace", "plan", "attend", "decode_fp8", "attend_fp8", "append_latent",
+__all__ = ["decode", "decode_noalloc", "Workspace", "plan", "attend", "decode_fp8", "attend_fp8", "append_latent",
            "append_latent_fp8",
            "absorb_prepare", "absorb_query", "up_project", "MlaError"]
 
@@ -142,6 +142,23 @@ def decode(q: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tenso
                          seq_lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
                          B, H, NB, BS, M, ws.ptr, ws.nbytes, _stream())
     _lib._check("mla_decode", st)
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, latent_cache: torch.Tensor, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                   lse: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """decode() without a workspace: the library's own per-GPU scratch array
+    holds the plan and partials, so the call allocates nothing (out and lse
+    are the caller's).  Calls on one GPU must not overlap."""
+    B, H, NB, BS, M = _check_inputs(q, latent_cache, block_table, seq_lens)
+    _check_outputs(out, lse, B, H)
+    _one_gpu(q=q, latent_cache=latent_cache, block_table=block_table, seq_lens=seq_lens,
+             out=out, lse=lse)
+    st = _lib.mla_decode_noalloc(q.data_ptr(), latent_cache.data_ptr(), block_table.data_ptr(),
+                                 seq_lens.data_ptr(), float(scale), out.data_ptr(), lse.data_ptr(),
+                                 B, H, NB, BS, M, _stream())
+    _lib._check("mla_decode_noalloc", st)
     return out, lse
 
 

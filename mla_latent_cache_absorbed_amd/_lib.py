@@ -37,6 +37,7 @@ SIGNATURES = {
     "mla_decode_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "mla_decode": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_decode_plan": (_I, [_P, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "mla_decode_noalloc": (_I, [_P, _P, _P, _P, _F, _P, _P, _I, _I, _I, _I, _I, _P]),
     "mla_decode_attend": (_I, [_P, _P, _P, _F, _P, _P, _I, _I, _I, _I, _I, _P, _S, _P]),
     "mla_decode_read_error": (_I, [_P, ctypes.POINTER(ctypes.c_int32), _P]),
     "mla_status_string": (ctypes.c_char_p, [_I]),
@@ -95,6 +96,12 @@ def mla_decode(q, latent_cache, block_table, seq_lens, scale, out, lse,
                B, H, NB, BS, M, workspace, workspace_bytes, stream) -> int:
     return lib().mla_decode(q, latent_cache, block_table, seq_lens, scale, out, lse,
                             B, H, NB, BS, M, workspace, workspace_bytes, stream)
+
+
+def mla_decode_noalloc(q, latent_cache, block_table, seq_lens, scale, out, lse,
+                       B, H, NB, BS, M, stream) -> int:
+    return lib().mla_decode_noalloc(q, latent_cache, block_table, seq_lens, scale, out, lse,
+                                    B, H, NB, BS, M, stream)
 
 
 def mla_decode_plan(seq_lens, B, H, M, BS, chunk_tokens, workspace, workspace_bytes,

@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/mla_decode.h"
 
 namespace {
@@ -77,10 +79,11 @@ struct WsLayout {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline WsLayout ws_layout(int B, int H) {
+// cap: work items the layout holds (default B + kMaxExtraItems)
+__host__ __device__ inline WsLayout ws_layout(int B, int H, int cap = -1) {
   WsLayout w;
   const int hp = heads_padded(H);
-  w.cap = B + kMaxExtraItems;
+  w.cap = cap < 0 ? B + kMaxExtraItems : cap;
   w.req_off = kHdrBytes;
   w.ctr_off = align256(w.req_off + size_t(B) * 16);
   w.big_off = align256(w.ctr_off + size_t(B) * kCtr * 4);
@@ -2299,9 +2302,7 @@ mla_status validate_attend_fp8(const void* q, const void* latent_cache, const in
 
 AttendArgs attend_args(const void* q, const void* latent_cache, const int32_t* block_table,
                        float scale, float kv_scale, void* out, float* lse, int32_t B, int32_t H,
-                       int32_t NB, int32_t BS, int32_t M, void* workspace) {
-  const WsLayout L = ws_layout(B, H);
-  char* ws = static_cast<char*>(workspace);
+                       int32_t NB, int32_t BS, int32_t M, const WsLayout& L, char* ws) {
   AttendArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.cache = static_cast<const __bf16*>(latent_cache);
@@ -2342,6 +2343,93 @@ mla_status validate_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t 
   return MLA_OK;
 }
 
+// The plan kernel over a workspace of layout L at ws.
+mla_status launch_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t M, int32_t BS,
+                       int32_t chunk_tokens, const WsLayout& L, char* ws, hipStream_t st) {
+  int ncu = 0, nxcd = 1;
+  mla_status s;
+  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  if ((s = device_xcd_count(&nxcd)) != MLA_OK) return s;
+  const Variant v = pick_variant(H);
+  // the wide kernels take their first items in workgroup order, so pairs
+  // placed nx apart land on one XCD; the narrow kernel's workers do not
+  const int nx = v.nw ? nxcd : 1;
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st,
+                     seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.workers_per_cu,
+                     (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req, nx,
+                     reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
+                     reinterpret_cast<int32_t*>(ws + L.ctr_off),
+                     reinterpret_cast<int32_t*>(ws + L.big_off),
+                     reinterpret_cast<int4*>(ws + L.item_off));
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// The attend kernel (bf16 cache) over a workspace of layout L at ws.
+mla_status launch_attend_bf16(const void* q, const void* latent_cache, const int32_t* block_table,
+                              float scale, void* out, float* lse, int32_t B, int32_t H, int32_t NB,
+                              int32_t BS, int32_t M, const WsLayout& L, char* ws, hipStream_t st) {
+  int ncu = 0;
+  mla_status s;
+  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
+  const AttendArgs a = attend_args(q, latent_cache, block_table, scale, 1.0f, out, lse, B, H, NB,
+                                   BS, M, L, ws);
+  const Variant v = pick_variant(H);
+  const int grid = ncu;  // one workgroup per compute unit
+  hipError_t e;
+  switch (v.nw) {
+    case 4: e = launch_attend<4, 4>(a, grid, st); break;
+    case 2: e = launch_attend<2, 4>(a, grid, st); break;
+    default:
+      if (a.lgBS >= 5)
+        hipLaunchKernelGGL(mla_attend_narrow_kernel<true>, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL(mla_attend_narrow_kernel<false>, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
+      e = hipGetLastError();
+      break;
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// The decode without a workspace argument: its plan and split partials live
+// in this file-scope array, one per GPU the library runs on, held until the
+// process ends.  Host code reaches it only through the device address that
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;  // 64 MiB
+static __device__ __align__(256) char scratch[kScratchBytes];
+void* g_scratch[kMaxDevices];  // device address of scratch on each device (null: not taken yet)
+std::mutex g_scratch_mu;
+
+mla_status scratch_address(void** p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return MLA_ERR_HIP;
+    g_scratch[dev] = a;
+  }
+  *p = g_scratch[dev];
+  return MLA_OK;
+}
+
+// The largest work-item capacity (at most B + kMaxExtraItems) whose layout
+// fits the scratch array; below B the batch does not fit at all.
+int scratch_cap(int B, int H) {
+  int hi = B + kMaxExtraItems;
+  if (ws_layout(B, H, hi).total <= kScratchBytes) return hi;
+  int lo = -1;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (ws_layout(B, H, mid).total <= kScratchBytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2356,23 +2444,8 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_
                            size_t workspace_bytes, void* stream) {
   mla_status s = validate_plan(seq_lens, B, H, M, BS, chunk_tokens, workspace, workspace_bytes);
   if (s != MLA_OK || B == 0) return s;
-  int ncu = 0, nxcd = 1;
-  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
-  if ((s = device_xcd_count(&nxcd)) != MLA_OK) return s;
-  const WsLayout L = ws_layout(B, H);
-  const Variant v = pick_variant(H);
-  // the wide kernels take their first items in workgroup order, so pairs
-  // placed nx apart land on one XCD; the narrow kernel's workers do not
-  const int nx = v.nw ? nxcd : 1;
-  char* ws = static_cast<char*>(workspace);
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream,
-                     seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.workers_per_cu,
-                     (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req, nx,
-                     reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
-                     reinterpret_cast<int32_t*>(ws + L.ctr_off),
-                     reinterpret_cast<int32_t*>(ws + L.big_off),
-                     reinterpret_cast<int4*>(ws + L.item_off));
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return launch_plan(seq_lens, B, H, M, BS, chunk_tokens, ws_layout(B, H),
+                     static_cast<char*>(workspace), (hipStream_t)stream);
 }
 
 mla_status mla_decode_attend(const void* q, const void* latent_cache,
@@ -2382,26 +2455,8 @@ mla_status mla_decode_attend(const void* q, const void* latent_cache,
   mla_status s = validate_attend(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
                                  workspace, workspace_bytes);
   if (s != MLA_OK || B == 0) return s;
-  int ncu = 0;
-  if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
-  const AttendArgs a = attend_args(q, latent_cache, block_table, scale, 1.0f, out, lse, B, H, NB,
-                                   BS, M, workspace);
-  const Variant v = pick_variant(H);
-  const int grid = ncu;  // one workgroup per compute unit
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  switch (v.nw) {
-    case 4: e = launch_attend<4, 4>(a, grid, st); break;
-    case 2: e = launch_attend<2, 4>(a, grid, st); break;
-    default:
-      if (a.lgBS >= 5)
-        hipLaunchKernelGGL(mla_attend_narrow_kernel<true>, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
-      else
-        hipLaunchKernelGGL(mla_attend_narrow_kernel<false>, dim3(grid), dim3(kNarrowWaves * 64), 0, st, a);
-      e = hipGetLastError();
-      break;
-  }
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return launch_attend_bf16(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M,
+                            ws_layout(B, H), static_cast<char*>(workspace), (hipStream_t)stream);
 }
 
 mla_status mla_decode(const void* q, const void* latent_cache, const int32_t* block_table,
@@ -2419,6 +2474,31 @@ mla_status mla_decode(const void* q, const void* latent_cache, const int32_t* bl
                            workspace, workspace_bytes, stream);
 }
 
+mla_status mla_decode_noalloc(const void* q, const void* latent_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, float scale, void* out, float* lse,
+                              int32_t B, int32_t H, int32_t NB, int32_t BS, int32_t M, void* stream) {
+  // the argument checks of mla_decode, with the scratch array's layout in
+  // place of a caller's workspace; nothing is enqueued on failure
+  mla_status s = check_sizes(B, H, M, BS);
+  if (s != MLA_OK) return s;
+  if (NB < 1) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !latent_cache || !block_table || !seq_lens || !out || !lse) return MLA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(latent_cache, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_ALIGNMENT;
+  if (!isfinite(scale) || !isfinite(scale_log2(scale, 1.0f))) return MLA_ERR_BAD_SCALE;
+  const int cap = scratch_cap(B, H);
+  if (cap < B) return MLA_ERR_WORKSPACE;  // the batch needs more than the scratch array holds
+  void* base = nullptr;
+  if ((s = scratch_address(&base)) != MLA_OK) return s;
+  const WsLayout L = ws_layout(B, H, cap);
+  char* ws = static_cast<char*>(base);
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = launch_plan(seq_lens, B, H, M, BS, 0, L, ws, st)) != MLA_OK) return s;
+  return launch_attend_bf16(q, latent_cache, block_table, scale, out, lse, B, H, NB, BS, M, L, ws, st);
+}
+
 mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache,
                                  const int32_t* block_table, float scale, float kv_scale,
                                  void* out, float* lse, int32_t B, int32_t H, int32_t NB,
@@ -2430,7 +2510,7 @@ mla_status mla_decode_attend_fp8(const void* q, const void* latent_cache,
   int ncu = 0;
   if ((s = device_cu_count(&ncu)) != MLA_OK) return s;
   const AttendArgs a = attend_args(q, latent_cache, block_table, scale, kv_scale, out, lse, B, H,
-                                   NB, BS, M, workspace);
+                                   NB, BS, M, ws_layout(B, H), static_cast<char*>(workspace));
   hipStream_t st = (hipStream_t)stream;
   // wide kernels: eight fp8 stages and the two weight buffers fill the 160
   // KiB of LDS; narrow kernel (H <= 32): two fp8 stages per wave slot

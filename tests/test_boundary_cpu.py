@@ -273,3 +273,36 @@ def test_overflowing_score_factor_is_rejected_on_host(L):
     if _no_device():
         assert _decode(scale=1e30) == _lib.MLA_ERR_HIP
         assert _decode8(scale=1e20, kv=1e10) == _lib.MLA_ERR_HIP
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, cache=FAKE, table=FAKE, lens=FAKE, scale=0.07, out=FAKE, lse=FAKE,
+             B=2, H=128, NB=14, BS=16, M=7, stream=None)
+    a.update(kw)
+    return _lib.mla_decode_noalloc(a["q"], a["cache"], a["table"], a["lens"], a["scale"],
+                                   a["out"], a["lse"], a["B"], a["H"], a["NB"], a["BS"], a["M"],
+                                   a["stream"])
+
+
+def test_noalloc_decode_rejects_bad_arguments_on_host(L):
+    """The entry point without a workspace makes mla_decode's host checks,
+    and rejects a batch whose plan and partials do not fit its fixed scratch
+    array (at 128 heads, more than 255 requests) before any HIP call."""
+    assert _noalloc(B=0) == _lib.MLA_OK
+    assert _noalloc(q=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _noalloc(lens=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _noalloc(out=None) == _lib.MLA_ERR_NULL_POINTER
+    assert _noalloc(H=129) == _lib.MLA_ERR_UNSUPPORTED
+    assert _noalloc(BS=24) == _lib.MLA_ERR_UNSUPPORTED
+    assert _noalloc(NB=0) == _lib.MLA_ERR_BAD_SHAPE
+    assert _noalloc(scale=float("nan")) == _lib.MLA_ERR_BAD_SCALE
+    assert _noalloc(scale=3.0e38) == _lib.MLA_ERR_BAD_SCALE
+    assert _noalloc(lens=FAKE + 2) == _lib.MLA_ERR_ALIGNMENT
+    assert _noalloc(out=FAKE + 8) == _lib.MLA_ERR_ALIGNMENT
+    # the scratch array holds 255 requests' partials at 128 heads
+    assert _noalloc(B=256, H=128) == _lib.MLA_ERR_WORKSPACE
+    assert _noalloc(B=100000, H=16) == _lib.MLA_ERR_WORKSPACE
+    if _no_device():
+        # sizes that fit reach the device query, which fails without a GPU
+        assert _noalloc(B=255, H=128) == _lib.MLA_ERR_HIP
+        assert _noalloc(B=900, H=16) == _lib.MLA_ERR_HIP
