@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MLA decode: cached-token reads/s, achieved HBM TB/s, % of roofline"
-COUNTERS = os.path.join(ROOT, "profiles", "attend_dp_rank_hbm_counters.json")
+PROFILES = os.path.join(ROOT, "profiles")
 SRC = os.path.join(ROOT, "mla_latent_cache_absorbed_amd", "csrc", "mla_decode.hip")
 
 
@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="dp_rank",
-                   choices=["dp_rank", "tp_slice", "ragged", "step61"])
+                   choices=["dp_rank", "tp_slice", "ragged", "step61", "dp_rank_fp8"])
     p.add_argument("--copies", type=int, default=3, help="independent caches rotated")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="budget of the CPU oracle sample")
@@ -59,6 +59,10 @@ def parse():
                    help="skip the fp8, append, absorption and attainable-peak records")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--profile-dir", default=None,
+                   help="write the profiles/ summaries of --workload from the rocprofv3 output "
+                        "directories under this one (kt, fetch, write, mfma, copy_fetch, "
+                        "copy_write), then exit (no GPU needed)")
     return p.parse_args()
 
 
@@ -74,18 +78,81 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
+def counter_record_path(name: str) -> str:
+    return os.path.join(PROFILES, f"attend_{name}_hbm_counters.json")
+
+
 def hbm_traffic_record(name: str):
-    """Counter-measured HBM bytes per attend launch, if taken on this source
-    and this workload."""
-    if name != "dp_rank":
-        return None
+    """Counter-measured HBM bytes per attend launch on this workload, if the
+    record was taken on this source (else None)."""
     try:
-        rec = json.load(open(COUNTERS))
+        rec = json.load(open(counter_record_path(name)))
     except (OSError, ValueError):
         return None
     if rec.get("src_sha256_16") != src_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def _rocprof_rows(d: str, suffix: str):
+    """Rows of every rocprofv3 CSV under directory d whose name ends with suffix."""
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def counter_means(d: str, kernel_prefix: str) -> dict:
+    """Per-dispatch means of every counter rocprofv3 --pmc collected under d
+    for kernels whose name starts with kernel_prefix: {counter: (mean, n)}.
+    A counter's value for one dispatch is the sum over the rows rocprofv3
+    writes for it."""
+    per = {}
+    for r in _rocprof_rows(d, "counter_collection.csv"):
+        if not r.get("Kernel_Name", "").startswith(kernel_prefix):
+            continue
+        key = (r["Counter_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (c, _), v in per.items():
+        s, n = out.get(c, (0.0, 0))
+        out[c] = (s + v, n + 1)
+    return {c: (s / n, n) for c, (s, n) in out.items()}
+
+
+def write_counter_record(name: str, fetch_dir: str, write_dir: str, cfetch_dir: str,
+                         cwrite_dir: str, kernel_prefix: str, commands: list) -> dict:
+    """The traffic record bench.py reports as roofline.traffic for a workload:
+    FETCH_SIZE and WRITE_SIZE (KiB per attend dispatch) scaled by what the
+    same counters read for a plain 1 GiB device copy, per attend launch."""
+    from mla_latent_cache_absorbed_amd import accounting as acc
+    from mla_latent_cache_absorbed_amd import workloads as wl
+    f = counter_means(fetch_dir, kernel_prefix)["FETCH_SIZE"]
+    w = counter_means(write_dir, kernel_prefix)["WRITE_SIZE"]
+    cf = counter_means(cfetch_dir, "__amd_rocclr_copyBuffer")["FETCH_SIZE"][0]
+    cw = counter_means(cwrite_dir, "__amd_rocclr_copyBuffer")["WRITE_SIZE"][0]
+    n = 1 << 30
+    fetch_scale = n / (cf * 1024.0)
+    write_scale = n / (cw * 1024.0)
+    sp = wl.spec("dp_rank" if name == "dp_rank_fp8" else name)
+    rec = {"kernel": kernel_prefix, "workload": name, "src_sha256_16": src_hash(),
+           "commands": commands, "R": "the repository root",
+           "attend_dispatches": {"fetch": f[1], "write": w[1]},
+           "attend_FETCH_SIZE_KiB_per_dispatch": f[0], "attend_WRITE_SIZE_KiB_per_dispatch": w[0],
+           "copy_probe": {"bytes_read": n, "bytes_written": n, "kernel": "__amd_rocclr_copyBuffer",
+                          "FETCH_SIZE_KiB": cf, "WRITE_SIZE_KiB": cw},
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "read_bytes_per_launch": f[0] * 1024.0 * fetch_scale,
+           "write_bytes_per_launch": w[0] * 1024.0 * write_scale}
+    rec["traffic_bytes_per_launch"] = rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    rec["algorithmic_bytes_per_launch"] = acc.algorithmic_bytes(
+        list(sp.seq_lens), sp.H, sp.BS, row_bytes=576 if name == "dp_rank_fp8" else 1152)
+    with open(counter_record_path(name), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
 
 
 def cpu_baseline(w, budget_s: float):
@@ -380,8 +447,233 @@ def fp8_record(w, layers_copies: int, steps: int, warmup: int, prewarm_ms: float
             "hbm_frac": gbs / HBM_PEAK_GBS, "mfma_tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS}
 
 
+def make_copies(name: str, copies: int, dev):
+    """The workload's inputs on the device: `copies` independent caches (and
+    queries) over one table and length vector, rotated by the timed steps so
+    that no call finds its cache in the 256 MB Infinity Cache; step61 holds
+    its 61 layers instead."""
+    import torch
+    from mla_latent_cache_absorbed_amd import workloads as wl
+    fp8 = name == "dp_rank_fp8"   # the DP-rank workload over FP8 copies of its caches
+    if fp8:
+        name = "dp_rank"
+    spec = wl.spec(name)
+    ncopies = spec.layers if name == "step61" else max(1, copies)
+    print(f"[bench] generating {ncopies} x {name} on {torch.cuda.get_device_name(0)}",
+          file=sys.stderr, flush=True)
+    wls = []
+    for i in range(ncopies):
+        if name == "step61":
+            w = wl.make(name, device=dev, seed=0, layer=i)
+        elif i == 0:
+            w = wl.make(name, device=dev, seed=0)
+        else:  # extra copies: same table and lengths, fresh q and cache
+            base = wls[0]
+            g = torch.Generator(device=dev).manual_seed(1000 + i)
+            q = torch.randn(base.q.shape, generator=g, device=dev).to(torch.bfloat16)
+            c = torch.randn(base.cache.shape, generator=g, device=dev).to(torch.bfloat16)
+            w = wl.Workload(name, q, c, base.block_table, base.seq_lens, base.scale)
+        if fp8:
+            w = wl.Workload(w.name, w.q, wl.fp8_cache(w.cache, wl.DEFAULT_KV_SCALE), w.block_table,
+                            w.seq_lens, w.scale)
+        wls.append(w)
+    torch.cuda.synchronize()
+    return wls
+
+
+def measure(wls, steps: int, warmup: int, prewarm_ms: float) -> dict:
+    """Timed decode steps over the workload: one step is one plan and one
+    attend per layer (step61: 61 layers, each on its own cache), all on the
+    current stream.  Untimed steps for prewarm_ms, then `warmup` steps, then
+    `steps` steps between two events; HIP events also bracket every attend
+    launch (on the stream the kernel runs on)."""
+    import torch
+    import mla_latent_cache_absorbed_amd as mla
+    from mla_latent_cache_absorbed_amd import workloads as wl
+    w0 = wls[0]
+    layers = wl.spec(w0.name).layers if w0.name in wl.NAMES else 1
+    B, H, M, BS = w0.B, w0.H, w0.M, w0.BS
+    dev = w0.q.device
+    ws = mla.Workspace(B, H, M, BS, dev)
+    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    fp8 = w0.cache.dtype == torch.uint8
+
+    def step(i, ev=None):
+        mla.plan(w0.seq_lens, H, M, BS, ws)
+        for l in range(layers):
+            w = wls[(i * layers + l) % len(wls)]
+            if ev is not None:
+                ev[0].record()
+            if fp8:
+                mla.attend_fp8(w.q, w.cache, w.block_table, w.scale, wl.DEFAULT_KV_SCALE, out, lse, ws)
+            else:
+                mla.attend(w.q, w.cache, w.block_table, w.scale, out, lse, ws)
+            if ev is not None:
+                ev[1].record()
+                ev.pop(0)
+                ev.pop(0)
+
+    # bring the GPU from idle to its loaded clock (steps take ~2x longer for
+    # the first ~10 ms), then the warm-up steps
+    n_pre = prewarm(step, prewarm_ms) if prewarm_ms > 0 else 0
+    for i in range(warmup):
+        step(n_pre + i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    n_attend = steps * layers
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_attend)]
+    pairs = [(evs[2 * j], evs[2 * j + 1]) for j in range(n_attend)]
+    queue = [e for p in pairs for e in p]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(n_pre + warmup + i, queue)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    attend_ms = sorted(a.elapsed_time(b) for a, b in pairs)
+    return {"layers": layers, "ms_step": start.elapsed_time(stop) / steps, "fp8": fp8,
+            "attend_avg_ms": sum(attend_ms) / len(attend_ms),
+            "attend_median_ms": attend_ms[len(attend_ms) // 2], "attend_min_ms": attend_ms[0],
+            "hdr": ws.header(), "prewarm_steps": n_pre}
+
+
+def workload_config(name: str, w0, layers: int, copies: int, prewarm_steps: int) -> dict:
+    seq = w0.seq_lens_list()
+    return {"workload": name, "batch": w0.B,
+            "seq_lens": "4096 each" if name in ("dp_rank", "tp_slice", "step61") else f"sum {sum(seq)}",
+            "heads": w0.H, "block_size": w0.BS, "blocks": w0.NB, "layers": layers,
+            "cache_copies": copies, "prewarm_steps": prewarm_steps}
+
+
+def workload_record(name: str, w0, m: dict) -> dict:
+    """Roofline record of the attend kernel on the workload: algorithmic
+    bytes and flops of one launch (one layer) over the mean launch time."""
+    from mla_latent_cache_absorbed_amd import accounting as acc
+    seq = w0.seq_lens_list()
+    H, BS, layers = w0.H, w0.BS, m["layers"]
+    alg_bytes = acc.algorithmic_bytes(seq, H, BS, row_bytes=576 if m["fp8"] else 1152)
+    alg_flops = acc.algorithmic_flops(seq, H)
+    t = m["attend_avg_ms"] * 1e-3
+    achieved_gbs = alg_bytes / t / 1e9
+    tflops = alg_flops / t / 1e12
+    intensity = alg_flops / alg_bytes
+    bound = "hbm" if intensity < MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    roof_t = max(alg_bytes / (HBM_PEAK_GBS * 1e9), alg_flops / (MFMA_BF16_PEAK_TFS * 1e12))
+    ms_step = m["ms_step"]
+    return {
+        "achieved_hbm_tb_s": layers * alg_bytes / (ms_step * 1e-3) / 1e12,
+        "roofline_frac_step": roof_t * layers / (ms_step * 1e-3),
+        "roofline": {
+            "bound": bound,
+            "kernel": ("mla_attend_narrow_kernel" if H <= 32 else "mla_attend_kernel")
+            + ("<fp8>" if m["fp8"] else ""),
+            "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": hbm_traffic_record(name),
+            "launch_ms": m["attend_avg_ms"],
+            "launch_ms_median": m["attend_median_ms"],
+            "launch_ms_min": m["attend_min_ms"],
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "mfma_tflops": tflops,
+            "mfma_frac": tflops / MFMA_BF16_PEAK_TFS,
+            "intensity_flop_per_byte": intensity,
+        },
+        "plan": {"items": m["hdr"][0], "chunk_tokens": m["hdr"][1]},
+    }
+
+
+ATTEND_KERNELS = {  # name prefix (as rocprofv3 reports it) of the attend kernel each workload runs
+    "dp_rank": "void (anonymous namespace)::mla_attend_kernel<4, 4, true, false>",
+    "ragged": "void (anonymous namespace)::mla_attend_kernel<4, 4, true, false>",
+    "step61": "void (anonymous namespace)::mla_attend_kernel<4, 4, true, false>",
+    "tp_slice": "void (anonymous namespace)::mla_attend_narrow_kernel<true, false>",
+    "dp_rank_fp8": "void (anonymous namespace)::mla_attend_kernel<4, 8, true, true>",
+}
+
+
+def profile_commands(name: str) -> dict:
+    """The rocprofv3 commands whose output --profile-dir summarises, with R
+    the repository root and O the output directory."""
+    run = f"python -u $R/bench.py --workload {name} --no-cpu --no-extras"
+    pre = "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 240 rocprofv3"
+    return {
+        "kt": f"{pre} --kernel-trace --stats -d $O/kt -o kt --output-format csv -- {run} --steps 20 --warmup 5",
+        "fetch": f"{pre} --pmc FETCH_SIZE -d $O/fetch -o p --output-format csv -- {run} --steps 3 --warmup 1 --prewarm-ms 0",
+        "write": f"{pre} --pmc WRITE_SIZE -d $O/write -o p --output-format csv -- {run} --steps 3 --warmup 1 --prewarm-ms 0",
+        "mfma": f"{pre} --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 -d $O/mfma -o p --output-format csv -- {run} --steps 3 --warmup 1 --prewarm-ms 0",
+        "copy_fetch": f"{pre} --pmc FETCH_SIZE -d $O/copy_fetch -o p --output-format csv -- python -u $R/bench.py --copy-probe",
+        "copy_write": f"{pre} --pmc WRITE_SIZE -d $O/copy_write -o p --output-format csv -- python -u $R/bench.py --copy-probe",
+    }
+
+
+def write_profiles(name: str, d: str) -> None:
+    """profiles/ summaries of one workload from rocprofv3 output under d: the
+    HBM-traffic record bench.py reads, a kernel-trace table and the MFMA
+    counters of the attend kernel."""
+    from mla_latent_cache_absorbed_amd import accounting as acc
+    from mla_latent_cache_absorbed_amd import workloads as wl
+    cmds = profile_commands(name)
+    kp = ATTEND_KERNELS[name]
+    sub = lambda k: os.path.join(d, k)  # noqa: E731
+    rec = write_counter_record(name, sub("fetch"), sub("write"), sub("copy_fetch"), sub("copy_write"),
+                               kp, [cmds[k] for k in ("fetch", "write", "copy_fetch", "copy_write")])
+    sp = wl.spec("dp_rank" if name == "dp_rank_fp8" else name)
+    seq = list(sp.seq_lens)
+    alg_bytes = acc.algorithmic_bytes(seq, sp.H, sp.BS, row_bytes=576 if name == "dp_rank_fp8" else 1152)
+    alg_flops = acc.algorithmic_flops(seq, sp.H)
+    stats = _rocprof_rows(sub("kt"), "kernel_stats.csv")
+    lines = [f"# Attend kernel, {name} workload ({sp.B} requests, {sp.H} heads, BS {sp.BS}, "
+             f"{sp.layers} layer(s)): kernel trace and counters", "",
+             "Commands, on one MI355X, with `R` the repository root and `O` an output directory:", "",
+             "```"] + [cmds[k] for k in ("kt", "fetch", "write", "mfma", "copy_fetch", "copy_write")] + \
+            ["```", "", f"Source hash (sha256, first 16 hex of mla_decode.hip): `{src_hash()}`", "",
+             "| kernel | calls | average ns | min ns | max ns | % of GPU time |", "|---|---|---|---|---|---|"]
+    att = None
+    for r in stats:
+        nm = r.get("Name", r.get("KernelName", ""))
+        short = nm if len(nm) < 70 else nm[:67] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                     f"{float(r['MaxNs']):.0f} | {float(r['Percentage']):.2f} |")
+        if nm.startswith(kp):
+            att = float(r["AverageNs"])
+    lines += ["", f"Algorithmic bytes per attend launch: {alg_bytes:,} B; flops {alg_flops:.4e}."]
+    if att:
+        lines.append(f"At the trace's average attend duration ({att / 1e3:.1f} us): "
+                     f"{alg_bytes / att:.0f} GB/s ({alg_bytes / att / HBM_PEAK_GBS * 100:.1f} % of 8 TB/s), "
+                     f"{alg_flops / att / 1e3:.0f} TFLOP/s.")
+    lines += ["", "HBM traffic of one attend launch (counters, scaled by a 1 GiB copy's reading):", "",
+              f"* FETCH_SIZE {rec['attend_FETCH_SIZE_KiB_per_dispatch']:.1f} KiB per dispatch x "
+              f"{rec['fetch_scale']:.4f} = {rec['read_bytes_per_launch']:,.0f} B read",
+              f"* WRITE_SIZE {rec['attend_WRITE_SIZE_KiB_per_dispatch']:.1f} KiB per dispatch x "
+              f"{rec['write_scale']:.4f} = {rec['write_bytes_per_launch']:,.0f} B written",
+              f"* total {rec['traffic_bytes_per_launch']:,.0f} B = "
+              f"{rec['traffic_bytes_per_launch'] / alg_bytes:.3f} x the algorithmic bytes"]
+    mf = counter_means(sub("mfma"), kp)
+    if mf:
+        busy, n = mf["SQ_VALU_MFMA_BUSY_CYCLES"]
+        gui = mf["GRBM_GUI_ACTIVE"][0]
+        mops = mf["SQ_INSTS_VALU_MFMA_MOPS_BF16"][0]
+        lines += ["", f"MFMA counters (means over {n} attend dispatches, summed over the 8 XCDs):", "",
+                  f"* SQ_INSTS_VALU_MFMA_MOPS_BF16 {mops:.4e} (x 512 = {mops * 512:.4e} flop; "
+                  f"algorithmic {alg_flops:.4e})",
+                  f"* SQ_VALU_MFMA_BUSY_CYCLES {busy:.4e}; GRBM_GUI_ACTIVE {gui:.4e} "
+                  f"({gui / 8:.4e} per XCD)",
+                  f"* MFMA busy = busy / (GUI per XCD x 1,024 SIMDs) = {busy / (gui / 8 * 1024) * 100:.1f} %"]
+    with open(os.path.join(PROFILES, f"mla_attend_{name}_profile.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main():
     args = parse()
+    if args.profile_dir:
+        write_profiles(args.workload, args.profile_dir)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
               "path has no multi-GPU code", file=sys.stderr)
@@ -396,89 +688,16 @@ def main():
 
     dev = torch.device("cuda:0")
     name = args.workload
-    spec = wl.spec(name)
-    layers = spec.layers
-    ncopies = layers if name == "step61" else max(1, args.copies)
-    print(f"[bench] generating {ncopies} x {name} on {torch.cuda.get_device_name(0)}",
-          file=sys.stderr, flush=True)
-    ws_list = []
-    wls = []
-    for i in range(ncopies):
-        w = wl.make(name, device=dev, seed=0, layer=i) if name == "step61" else \
-            wl.make(name, device=dev, seed=0) if i == 0 else None
-        if w is None:  # extra copies: same table and lengths, fresh q and cache
-            base = wls[0]
-            g = torch.Generator(device=dev).manual_seed(1000 + i)
-            q = torch.randn(base.q.shape, generator=g, device=dev).to(torch.bfloat16)
-            c = torch.randn(base.cache.shape, generator=g, device=dev).to(torch.bfloat16)
-            w = wl.Workload(name, q, c, base.block_table, base.seq_lens, base.scale)
-        wls.append(w)
+    wls = make_copies(name, args.copies, dev)
+    m = measure(wls, args.steps, args.warmup, args.prewarm_ms)
     w0 = wls[0]
     B, H, M, BS, NB = w0.B, w0.H, w0.M, w0.BS, w0.NB
-    ws = mla.Workspace(B, H, M, BS, dev)
-    out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     seq = w0.seq_lens_list()
-    torch.cuda.synchronize()
-
-    def step(i, ev=None):
-        # one decode step: plan, then one attend per layer
-        mla.plan(w0.seq_lens, H, M, BS, ws)
-        for l in range(layers):
-            w = wls[(i * layers + l) % len(wls)]
-            if ev is not None:
-                ev[0].record()
-            mla.attend(w.q, w.cache, w.block_table, w.scale, out, lse, ws)
-            if ev is not None:
-                ev[1].record()
-                ev.pop(0)
-                ev.pop(0)
-
-    # bring the GPU from idle to its loaded clock (steps take ~2x longer for
-    # the first ~10 ms), then the warm-up steps
-    n_pre = 0
-    if args.prewarm_ms > 0:
-        t_end = time.time() + args.prewarm_ms * 1e-3
-        while time.time() < t_end:
-            for _ in range(10):
-                step(n_pre)
-                n_pre += 1
-            torch.cuda.synchronize()
-    for i in range(args.warmup):
-        step(n_pre + i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    n_attend = args.steps * layers
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_attend)]
-    pairs = [(evs[2 * j], evs[2 * j + 1]) for j in range(n_attend)]
-    queue = [e for p in pairs for e in p]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(n_pre + args.warmup + i, queue)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    attend_ms = [a.elapsed_time(b) for a, b in pairs]
-    attend_avg_ms = sum(attend_ms) / len(attend_ms)
-    attend_sorted = sorted(attend_ms)
-    hdr = ws.header()
-
-    tokens_step = acc.token_reads(seq, layers)
-    value = tokens_step / (ms_step * 1e-3)
-    alg_bytes = acc.algorithmic_bytes(seq, H, BS)         # per attend launch (one layer)
-    alg_flops = acc.algorithmic_flops(seq, H)
-    achieved_gbs = alg_bytes / (attend_avg_ms * 1e-3) / 1e9
-    tflops = alg_flops / (attend_avg_ms * 1e-3) / 1e12
-    step_gbs = layers * alg_bytes / (ms_step * 1e-3) / 1e9
-    intensity = alg_flops / alg_bytes
-    bound = "hbm" if intensity < MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-    roof_t = max(alg_bytes / (HBM_PEAK_GBS * 1e9), alg_flops / (MFMA_BF16_PEAK_TFS * 1e12))
+    layers = m["layers"]
+    ms_step = m["ms_step"]
     rec = {
         "metric": METRIC,
-        "value": value,
+        "value": acc.token_reads(seq, layers) / (ms_step * 1e-3),
         "unit": "cached-token reads/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -489,36 +708,32 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "batch": B, "seq_lens": "4096 each" if name in
-                   ("dp_rank", "tp_slice", "step61") else f"sum {sum(seq)}",
-                   "heads": H, "block_size": BS, "blocks": NB, "layers": layers,
-                   "cache_copies": len(wls), "prewarm_steps": n_pre},
-        "achieved_hbm_tb_s": step_gbs / 1e3,
-        "roofline_frac_step": roof_t * layers / (ms_step * 1e-3),
-        "roofline": {
-            "bound": bound,
-            "kernel": "mla_attend_narrow_kernel" if H <= 32 else "mla_attend_kernel",
-            "achieved": achieved_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": hbm_traffic_record(name),
-            "launch_ms": attend_avg_ms,
-            "launch_ms_median": attend_sorted[len(attend_sorted) // 2],
-            "launch_ms_min": attend_sorted[0],
-            "algorithmic_bytes_per_launch": alg_bytes,
-            "mfma_tflops": tflops,
-            "mfma_frac": tflops / MFMA_BF16_PEAK_TFS,
-            "intensity_flop_per_byte": intensity,
-        },
-        "plan": {"items": hdr[0], "chunk_tokens": hdr[1]},
+        "config": workload_config(name, w0, layers, len(wls), m["prewarm_steps"]),
     }
+    rec.update(workload_record(name, w0, m))
+    if not args.no_extras and name == "dp_rank":
+        # the other workloads of the path, each measured the same way: one
+        # JSON object per workload with its own roofline record
+        rec["workloads"] = {}
+        for other in ("tp_slice", "ragged", "step61"):
+            print(f"[bench] {other}", file=sys.stderr, flush=True)
+            ow = make_copies(other, args.copies, dev)
+            om = measure(ow, args.steps, args.warmup, args.prewarm_ms)
+            o0 = ow[0]
+            orec = {"config": workload_config(other, o0, om["layers"], len(ow), om["prewarm_steps"]),
+                    "ms_per_step": om["ms_step"],
+                    "value": acc.token_reads(o0.seq_lens_list(), om["layers"]) / (om["ms_step"] * 1e-3),
+                    "unit": "cached-token reads/s"}
+            orec.update(workload_record(other, o0, om))
+            rec["workloads"][other] = orec
+            del ow, om, o0
+            torch.cuda.empty_cache()
     if not args.no_extras:
         if BS >= 32 and name != "step61":
             rec["fp8"] = fp8_record(w0, len(wls), args.steps, args.warmup, args.prewarm_ms)
         rec["append"] = append_record(w0, prewarm_ms=args.prewarm_ms)
         rec["absorb"] = absorb_record(B, H, prewarm_ms=args.prewarm_ms)
-        rec["attainable"] = attainable_peaks(achieved_gbs, tflops)
+        rec["attainable"] = attainable_peaks(rec["roofline"]["achieved"], rec["roofline"]["mfma_tflops"])
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
