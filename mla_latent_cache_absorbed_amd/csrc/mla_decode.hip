@@ -1086,6 +1086,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // KB; pad[h] moves the lanes of padding heads past the resource, so their
     // stores and loads are dropped without a branch
     const uint32_t slab = uint32_t(4 * CPW * w) * 1024 + uint32_t(lane_e) * 16;
+    const uint32_t slabp = uint32_t(2 * CPW * w) * 1024 + uint32_t(lane_e) * 16;  // bf16 half partials
     uint32_t pad[NW];
 #pragma unroll
     for (int h = 0; h < NW; ++h) pad[h] = (h * 32 + hl_e < a.H) ? 0u : 0x40000000u;
@@ -1115,7 +1116,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // the item over the first tokens) merges head blocks [s NW/2, (s+1)
     // NW/2) and publishes the other half for its partner, so each item
     // stores and loads half a partial and both halves of the output are
-    // written at once; no item waits for a ticket.  The request's two
+    // written at once; no item waits for a ticket.  The half goes out in
+    // bf16 (its own term stays fp32).  The request's two
     // counters become one publish word per item: 0 until the item's half is
     // out, then 1 + the XCD it ran on.  Halves are written through to memory
     // (sc1), so every reader sees them; a reader on the publisher's XCD
@@ -1131,18 +1133,22 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       const i32x4 rq = ((const CONST_AS i32x4*)a.req)[b];
       const int other = me ? ((0 < rq[1]) ? rq[0] : rq[2]) : ((1 < rq[1]) ? rq[0] + 1 : rq[2]);
       {
+        // the half goes out in bf16: 1 KB block pair (h, cb, p) holds, in
+        // lane l's 16 bytes, the values of blocks (h, cb, 2p) and (h, cb,
+        // 2p + 1) of that lane (the fp32 layout above, two blocks a lane)
         const __amdgpu_buffer_rsrc_t pr = part_rsrc(it);
 #pragma unroll
         for (int hh = 0; hh < kHalf; ++hh)
 #pragma unroll
           for (int c = 0; c < CPW; ++c)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int pp = 0; pp < 2; ++pp) {
               const int h = theirs0 + hh;
-              f32x4 v4;
+              bf16x8 v8;
 #pragma unroll
-              for (int r = 0; r < 4; ++r) v4[r] = o[h * CPW + c][4 * g + r] * inv[h];
-              __builtin_amdgcn_raw_buffer_store_b128(v4, pr, slab + pad[h] + (64 * h + 4 * c + g) * 1024, 0, kSc1);
+              for (int r = 0; r < 8; ++r) v8[r] = (__bf16)(o[h * CPW + c][8 * pp + r] * inv[h]);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v8), pr,
+                                                     slabp + pad[h] + (32 * h + 2 * c + pp) * 1024, 0, kSc1);
             }
         // every lane stores its head's log-sum-exp (the partner reads those of its half)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
@@ -1165,7 +1171,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       constexpr int kWB8 = kRing / NW / 1024 * 1024;
       constexpr int kWaveBuf = (kF8 && kWB8 < kStageBytes) ? kWB8 : kStageBytes;
       static_assert(NW * kWaveBuf <= kRing, "merge staging fits the ring");
-      constexpr int kBlocks = kHalf * CPW * 4;   // 1 KB blocks per wave
+      constexpr int kBlocks = kHalf * CPW * 2;   // 1 KB block pairs per wave
       static_assert(kBlocks * 1024 <= kWaveBuf, "one round of loads");
       char LDS_AS* mb = lds + w * kWaveBuf;
       const __amdgpu_buffer_rsrc_t pr = part_rsrc(other);
@@ -1174,9 +1180,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       if (near) {
 #pragma unroll
         for (int j = 0; j < kBlocks; ++j) {
-          const int hh = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+          const int hh = j / (2 * CPW), c = (j / 2) % CPW, pp = j % 2;
           const int h = mine0 + hh;
-          dma16_buffer_sc0(pr, slab + pad[h] + uint32_t(64 * h + 4 * c + g) * 1024, mb + j * 1024);
+          dma16_buffer_sc0(pr, slabp + pad[h] + uint32_t(32 * h + 2 * c + pp) * 1024, mb + j * 1024);
         }
 #pragma unroll
         for (int hh = 0; hh < kHalf; ++hh)
@@ -1185,9 +1191,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       } else {
 #pragma unroll
         for (int j = 0; j < kBlocks; ++j) {
-          const int hh = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+          const int hh = j / (2 * CPW), c = (j / 2) % CPW, pp = j % 2;
           const int h = mine0 + hh;
-          dma16_buffer(pr, slab + pad[h] + uint32_t(64 * h + 4 * c + g) * 1024, mb + j * 1024);
+          dma16_buffer(pr, slabp + pad[h] + uint32_t(32 * h + 2 * c + pp) * 1024, mb + j * 1024);
         }
 #pragma unroll
         for (int hh = 0; hh < kHalf; ++hh)
@@ -1220,24 +1226,29 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
         }
       }
       constexpr int kGroup = 8;
-      static_assert(kBlocks % kGroup == 0, "groups of blocks");
+      static_assert(kBlocks % kGroup == 0, "groups of block pairs");
 #pragma unroll
       for (int jg = 0; jg < kBlocks; jg += kGroup) {
-        f32x4 xs[kGroup];
+        bf16x8 xs[kGroup];
 #pragma unroll
-        for (int jj = 0; jj < kGroup; ++jj) xs[jj] = *(const f32x4 LDS_AS*)(mb + (jg + jj) * 1024 + lane_e * 16);
+        for (int jj = 0; jj < kGroup; ++jj) xs[jj] = *(const bf16x8 LDS_AS*)(mb + (jg + jj) * 1024 + lane_e * 16);
 #pragma unroll
         for (int jj = 0; jj < kGroup; ++jj) {
           const int j = jg + jj;
-          const int hh = j / (4 * CPW), c = (j / 4) % CPW, g = j % 4;
+          const int hh = j / (2 * CPW), c = (j / 2) % CPW, pp = j % 2;
           const int h = mine0 + hh;
-          float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float own = o[h * CPW + c][4 * g + r] * inv[h];
-            v[r] = me ? fmaf(wb[hh], own, wa[hh] * xs[jj][r]) : fmaf(wb[hh], xs[jj][r], wa[hh] * own);
+          for (int gi = 0; gi < 2; ++gi) {
+            const int g = 2 * pp + gi;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float own = o[h * CPW + c][4 * g + r] * inv[h];
+              const float oth = (float)xs[jj][4 * gi + r];
+              v[r] = me ? fmaf(wb[hh], own, wa[hh] * oth) : fmaf(wb[hh], oth, wa[hh] * own);
+            }
+            store_out4(h, c, g, v);
           }
-          store_out4(h, c, g, v);
         }
       }
       // the lse of this wave's head block, if that block is in this item's
