@@ -1923,7 +1923,9 @@ __global__ __launch_bounds__(kNarrowWaves * 64, 1) void mla_attend_narrow_kernel
 // ---------------------------------------------------------------------------
 // plan
 // ---------------------------------------------------------------------------
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanCands = 256;  // candidate chunk sizes
+constexpr int kPlanParts = kPlanThreads / kPlanCands;  // threads per candidate
 constexpr int kPlanLens = 4096;  // seq_lens staged in LDS per pass
 
 __device__ __forceinline__ int plan_candidate(int i) {
@@ -1934,27 +1936,54 @@ __device__ __forceinline__ int plan_candidate(int i) {
   return 32 * int(k);
 }
 
+// Wave-wide inclusive scans on DPP: row shifts by 1, 2, 4 and 8 scan each
+// row of 16 lanes, then the last lane of row 0 (row 2) is broadcast into
+// row 1 (row 3), and the last lane of row 1 into rows 2 and 3.  A lane whose
+// source is outside its row, or whose row the mask leaves out, keeps `old`,
+// the operation's identity.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, kCtrl, kRowMask, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_add(int x) {
+  x += dpp_i32<0x111, 0xf>(0, x);  // row_shr:1
+  x += dpp_i32<0x112, 0xf>(0, x);  // row_shr:2
+  x += dpp_i32<0x114, 0xf>(0, x);  // row_shr:4
+  x += dpp_i32<0x118, 0xf>(0, x);  // row_shr:8
+  x += dpp_i32<0x142, 0xa>(0, x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_i32<0x143, 0xc>(0, x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ unsigned long long dpp_min_u64(unsigned long long x) {
+  const int lo = dpp_i32<kCtrl, kRowMask>(-1, int(uint32_t(x)));
+  const int hi = dpp_i32<kCtrl, kRowMask>(-1, int(uint32_t(x >> 32)));
+  const unsigned long long y = (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+  return y < x ? y : x;
+}
+// the least of the wave's 64 values, in every lane
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long x) {
+  x = dpp_min_u64<0x111, 0xf>(x);
+  x = dpp_min_u64<0x112, 0xf>(x);
+  x = dpp_min_u64<0x114, 0xf>(x);
+  x = dpp_min_u64<0x118, 0xf>(x);
+  x = dpp_min_u64<0x142, 0xa>(x);
+  x = dpp_min_u64<0x143, 0xc>(x);
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(x)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(x >> 32)), 63);
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // Inclusive block-wide scan of four ints per thread; returns the inclusive
-// scan and the block totals.  A 64-lane shuffle scan in each wave, then the
-// four wave totals through LDS.
+// scan and the block totals.  A DPP scan in each wave, then the wave totals
+// through LDS.
 struct Scan4 {
   int4 incl, total;
 };
 __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  int4 x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y0 = __shfl_up(x.x, off, 64), y1 = __shfl_up(x.y, off, 64);
-    const int y2 = __shfl_up(x.z, off, 64), y3 = __shfl_up(x.w, off, 64);
-    if (lane >= off) {
-      x.x += y0;
-      x.y += y1;
-      x.z += y2;
-      x.w += y3;
-    }
-  }
+  const int4 x = make_int4(wave_incl_add(v.x), wave_incl_add(v.y), wave_incl_add(v.z), wave_incl_add(v.w));
   if (lane == 63) s_scan[wv] = x;
   __syncthreads();
   int4 pre = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
@@ -1972,7 +2001,6 @@ __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
     tot.z += t.z;
     tot.w += t.w;
   }
-  __syncthreads();
   Scan4 r;
   r.incl = make_int4(x.x + pre.x, x.y + pre.y, x.z + pre.z, x.w + pre.w);
   r.total = tot;
@@ -1987,8 +2015,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
     int ovh, int cap, int units_per_req, int nx, int32_t* __restrict__ hdr, int4* __restrict__ req,
     int32_t* __restrict__ ctr, int32_t* __restrict__ big, int4* __restrict__ items) {
-  __shared__ long long s_cost[kPlanThreads / 64];
-  __shared__ int s_chunk[kPlanThreads / 64];
+  __shared__ unsigned long long s_key[kPlanCands / 64];
+  __shared__ long long s_part[kPlanParts][kPlanCands];
   __shared__ int4 s_scan[kPlanThreads / 64];
   __shared__ __attribute__((aligned(16))) int s_len[kPlanLens];
   __shared__ __attribute__((aligned(16))) float s_m[kPlanLens];
@@ -2019,11 +2047,13 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   if (resident) bad = stage(0, B);
   auto len_of = [&](int b) { return resident ? s_len[b] : clamp_len(seq_lens[b]); };
 
-  // 1) chunk size: each thread prices one candidate,
-  //    cost = ceil(items / slots) * (chunk + per-item overhead).
+  // 1) chunk size: four threads price each of the kPlanCands candidates,
+  //    cost = ceil(items / slots) * (chunk + per-item overhead), each over a
+  //    quarter of the requests (every fourth group of four lengths).
   int chunk = forced;
   if (forced <= 0) {
-    const int T = plan_candidate(tid);
+    const int cand = tid % kPlanCands, part = tid / kPlanCands;
+    const int T = plan_candidate(cand);
     // ceil(L / T) for T = 32 d: ceil(ceil(L / 32) / d), with the quotient from
     // a float reciprocal (off by at most one for these sizes) and one exact
     // correction; this keeps integer division out of the B x 256 loop.
@@ -2039,9 +2069,10 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     };
     // Float form of the same count, four VALU ops per request: with m < 2^22
     // and 1/d within one ulp, fma(m, 1/d, -1/(2d)) lies within 1/(2d) of
-    // (m - 1/2) / d, so its ceiling is ceil(m / d) exactly.  The float sum is
-    // exact below 2^24 and stays at or above 2^24 (past any workspace cap)
-    // once the count gets there.  Padding entries (m = 0) count one each.
+    // (m - 1/2) / d, so its ceiling is ceil(m / d) exactly.  Each thread's
+    // float sum is exact below 2^24 and stays at or above 2^24 (past any
+    // workspace cap) once its count gets there.  Padding entries (m = 0)
+    // count one each.
     const bool fast = Lmax <= (1 << 26);
     const float inv_df = 1.0f / float(d);
     const float half_df = 0.5f * inv_df;
@@ -2053,51 +2084,45 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
       const int nb4 = (nb + 3) & ~3;
       if (fast) {
         float acc = 0.0f;
-#pragma unroll 4
-        for (int i = 0; i < nb4; i += 4) {
+#pragma unroll 2
+        for (int i = 4 * part; i < nb4; i += 4 * kPlanParts) {
           const float4 m4 = *reinterpret_cast<const float4*>(&s_m[i]);
           acc += (items_f(m4.x) + items_f(m4.y)) + (items_f(m4.z) + items_f(m4.w));
         }
-        n += (long long)acc - (nb4 - nb);
+        n += (long long)acc - (part == 0 ? nb4 - nb : 0);
       } else {
-#pragma unroll 4
-        for (int i = 0; i < nb4; i += 4) {
+#pragma unroll 2
+        for (int i = 4 * part; i < nb4; i += 4 * kPlanParts) {
           const int4 m4 = *reinterpret_cast<const int4*>(&s_len[i]);
           n += items_of(m4.x) + items_of(m4.y) + items_of(m4.z) + items_of(m4.w);
         }
       }
       if (!resident) __syncthreads();
     }
-    // cheapest candidate, the larger chunk on ties: a shuffle reduction in
-    // each wave, then over the four waves
-    long long c = (n <= cap) ? ((n + n_slots - 1) / n_slots) * (long long)(T + ovh) : (1ll << 62);
-    int k = T;
+    s_part[part][cand] = n;
+    __syncthreads();
+    if (part == 0) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const long long c2 = __shfl_xor(c, off, 64);
-      const int k2 = __shfl_xor(k, off, 64);
-      if (c2 < c || (c2 == c && k2 > k)) {
-        c = c2;
-        k = k2;
-      }
-    }
-    if ((tid & 63) == 0) {
-      s_cost[tid >> 6] = c;
-      s_chunk[tid >> 6] = k;
+      for (int p = 1; p < kPlanParts; ++p) n += s_part[p][cand];
+      // A count within the cap fits 32 bits, and so does its division.  The
+      // key orders candidates by cost, then by larger chunk (candidates
+      // grow with their index): cost * 256 + (255 - index), below 2^60;
+      // 2^62 marks a candidate whose items exceed the cap.
+      const unsigned long long cost =
+          (unsigned long long)((uint32_t(n) + uint32_t(n_slots) - 1u) / uint32_t(n_slots)) *
+          (unsigned long long)(T + ovh);
+      const unsigned long long key = (n <= cap) ? (cost << 8) | uint32_t(kPlanCands - 1 - cand) : (1ull << 62);
+      const unsigned long long wmin = wave_min_u64(key);
+      if ((tid & 63) == 0) s_key[tid >> 6] = wmin;
     }
     __syncthreads();
-    long long cb = s_cost[0];
-    int kb = s_chunk[0];
+    unsigned long long kmin = s_key[0];
 #pragma unroll
-    for (int i = 1; i < kPlanThreads / 64; ++i) {
-      if (s_cost[i] < cb || (s_cost[i] == cb && s_chunk[i] > kb)) {
-        cb = s_cost[i];
-        kb = s_chunk[i];
-      }
-    }
+    for (int i = 1; i < kPlanCands / 64; ++i) kmin = s_key[i] < kmin ? s_key[i] : kmin;
+    const int kb = plan_candidate(kPlanCands - 1 - int(kmin & 0xff));
     chunk = kb;
     // no candidate fits the workspace: one item per request
-    if (cb >= (1ll << 62)) chunk = ((Lmax + 31) / 32) * 32;
+    if (kmin >= (1ull << 62)) chunk = ((Lmax + 31) / 32) * 32;
   } else if (!resident) {
     for (int b0 = 0; b0 < B; b0 += kPlanLens) {
       bad |= stage(b0, min(kPlanLens, B - b0));
@@ -2105,76 +2130,116 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     }
   }
 
-  // 2) totals: requests split into exactly two items (pairs), and the full
-  //    chunks, remainders and empty requests of all other requests; the
-  //    range-check bits; the counters of every request start at 0
-  int4 loc = make_int4(0, 0, 0, 0);
-  for (int b = tid; b < B; b += kPlanThreads) {
-    const int L = len_of(b);
-    const int nf = L / chunk, nr = (L % chunk) ? 1 : 0;
-    const bool pair = nf + nr == 2;
-    loc.x += pair ? 0 : nf;
-    loc.y += pair ? 0 : nr;
-    loc.z += (L == 0) ? 1 : 0;
-    loc.w += pair ? 1 : 0;
-#pragma unroll
-    for (int k = 0; k < kCtr; ++k) ctr[kCtr * b + k] = 0;
-  }
-  const int4 tot = block_scan4(loc, s_scan).total;
-  const int NF = tot.x, NR = tot.y, NE = tot.z, NP = tot.w;
-  const int any_bad = __syncthreads_or(bad);
-  // Pairs come first.  The two items of pair j of the first nx * G pairs
-  // (G = NP / nx) sit nx positions apart, so that workgroups w and w + nx,
-  // which the dispatcher places on the same XCD, take them; the last
-  // NP % nx pairs follow side by side, then the other items in the order
-  // full chunks, remainders, empty requests.
-  const int G = NP / nx;
-  auto pair_pos = [&](int j, int half) {
+  // Pairs (requests split into exactly two items) come first.  The two
+  // items of pair j of the first nx * G pairs (G = NP / nx) sit nx
+  // positions apart, so that workgroups w and w + nx, which the dispatcher
+  // places on the same XCD, take them; the last NP % nx pairs follow side
+  // by side, then the other items in the order full chunks, remainders,
+  // empty requests.
+  int NF, NR, NE, NP, NBIG, any_bad;
+  auto pair_pos = [&](int j, int half, int G) {
     if (j < G * nx) return 2 * nx * (j / nx) + (j % nx) + half * nx;
     return 2 * j + half;
   };
-  const int Q0 = 2 * NP;  // first position of the other items
-
-  // 3) per-request placement from exclusive scans; requests split into
-  //    kMergeMinItems or more items are listed for the merge units
-  int4 carry = make_int4(0, 0, 0, 0);
-  int carry_big = 0;
-  for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
-    const int b = b0 + tid;
-    const int L = (b < B) ? len_of(b) : 0;
-    const int nf0 = L / chunk;
-    const int nr0 = (L % chunk) ? 1 : 0;
+  // Writes request b's record, its items and its merge-unit entry, given
+  // the exclusive prefix counts of the requests before it (full chunks,
+  // remainders, empties, pairs and widely split requests of the others).
+  auto place = [&](int b, int L, int4 pre, int pre_big) {
+    const int nf0 = L / chunk, nr0 = (L % chunk) ? 1 : 0;
     const int cnt = nf0 + nr0;
-    const bool pair = b < B && cnt == 2;
-    const int nf = pair ? 0 : nf0, nr = pair ? 0 : nr0;
-    const int ne = (b < B && L == 0) ? 1 : 0;
-    const int np = pair ? 1 : 0;
-    const int nbg = (b < B && cnt >= kMergeMinItems) ? 1 : 0;
-    const Scan4 sc = block_scan4(make_int4(nf, nr, ne, np), s_scan);
-    const Scan4 sb = block_scan4(make_int4(nbg, 0, 0, 0), s_scan);
-    const int big_incl = sb.incl.x;
-    if (b < B) {
-      if (pair) {
-        const int j = carry.w + sc.incl.w - 1;
-        const int p0 = pair_pos(j, 0), p1 = pair_pos(j, 1);
-        req[b] = make_int4(p0, 1, p1, 2);
-        items[p0] = make_int4(b, 0, chunk, 2);
-        items[p1] = make_int4(b, chunk, L, 2);
-      } else {
-        const int fbeg = Q0 + carry.x + sc.incl.x - nf;
-        const int ritem = nr ? (Q0 + NF + carry.y + sc.incl.y - nr) : -1;
-        req[b] = make_int4(fbeg, nf, ritem, cnt);
-        for (int s = 0; s < nf; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
-        if (nr) items[ritem] = make_int4(b, nf * chunk, L, cnt);
-        if (ne) items[Q0 + NF + NR + carry.z + sc.incl.z - 1] = make_int4(b, 0, 0, 0);
-        if (nbg) big[carry_big + big_incl - 1] = b;
-      }
+    const int Q0 = 2 * NP;  // first position of the other items
+    if (cnt == 2) {
+      const int G = NP / nx;
+      const int p0 = pair_pos(pre.w, 0, G), p1 = pair_pos(pre.w, 1, G);
+      req[b] = make_int4(p0, 1, p1, 2);
+      items[p0] = make_int4(b, 0, chunk, 2);
+      items[p1] = make_int4(b, chunk, L, 2);
+    } else {
+      const int fbeg = Q0 + pre.x;
+      const int ritem = nr0 ? (Q0 + NF + pre.y) : -1;
+      req[b] = make_int4(fbeg, nf0, ritem, cnt);
+      for (int s = 0; s < nf0; ++s) items[fbeg + s] = make_int4(b, s * chunk, (s + 1) * chunk, cnt);
+      if (nr0) items[ritem] = make_int4(b, nf0 * chunk, L, cnt);
+      if (L == 0) items[Q0 + NF + NR + pre.z] = make_int4(b, 0, 0, 0);
+      if (cnt >= kMergeMinItems) big[pre_big] = b;
     }
-    carry.x += sc.total.x;
-    carry.y += sc.total.y;
-    carry.z += sc.total.z;
-    carry.w += sc.total.w;
-    carry_big += sb.total.x;
+#pragma unroll
+    for (int k = 0; k < kCtr; ++k) ctr[kCtr * b + k] = 0;
+  };
+  // this request's counts (full chunks, remainders, empty, pair) and
+  // whether it is split widely enough for the merge units
+  auto counts = [&](int b, int L, int& nbg) {
+    const int nf0 = L / chunk, nr0 = (L % chunk) ? 1 : 0;
+    const bool pair = b < B && nf0 + nr0 == 2;
+    nbg = (b < B && nf0 + nr0 >= kMergeMinItems) ? 1 : 0;
+    return make_int4(pair ? 0 : nf0, pair ? 0 : nr0, (b < B && L == 0) ? 1 : 0, pair ? 1 : 0);
+  };
+
+  if (resident && B <= kPlanThreads) {
+    // 2) one pass: a single scan gives every request's prefix and the
+    //    totals.  With B <= 1024 every count and prefix fits 16 bits, so
+    //    the empty and widely-split counts share a word, as do the pair
+    //    count and the range-check bits.
+    const int b = tid;
+    const int L = (b < B) ? s_len[b] : 0;
+    int nbg;
+    const int4 c = counts(b, L, nbg);
+    const int4 packed = make_int4(c.x, c.y, c.z | (nbg << 16), c.w | ((b < B && bad) ? 1 << 16 : 0));
+    const Scan4 sc = block_scan4(packed, s_scan);
+    NF = sc.total.x;
+    NR = sc.total.y;
+    NE = sc.total.z & 0xffff;
+    NBIG = sc.total.z >> 16;
+    NP = sc.total.w & 0xffff;
+    any_bad = (sc.total.w >> 16) != 0;
+    if (b < B) {
+      const int4 pre = make_int4(sc.incl.x - c.x, sc.incl.y - c.y, (sc.incl.z & 0xffff) - c.z,
+                                 (sc.incl.w & 0xffff) - c.w);
+      place(b, L, pre, (sc.incl.z >> 16) - nbg);
+    }
+  } else {
+    // 2) totals: the items of pairs and of all other requests, empty
+    //    requests, widely split requests and the range-check bits
+    int4 loc = make_int4(0, 0, 0, 0);
+    int locbig = 0;
+    for (int b = tid; b < B; b += kPlanThreads) {
+      int nbg;
+      const int4 c = counts(b, len_of(b), nbg);
+      loc.x += c.x;
+      loc.y += c.y;
+      loc.z += c.z;
+      loc.w += c.w;
+      locbig += nbg;
+    }
+    const int4 tot = block_scan4(loc, s_scan).total;
+    NF = tot.x;
+    NR = tot.y;
+    NE = tot.z;
+    NP = tot.w;
+    NBIG = block_scan4(make_int4(locbig, 0, 0, 0), s_scan).total.x;
+    any_bad = __syncthreads_or(bad);
+    // 3) per-request placement from exclusive scans, kPlanThreads requests
+    //    at a time
+    int4 carry = make_int4(0, 0, 0, 0);
+    int carry_big = 0;
+    for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
+      const int b = b0 + tid;
+      const int L = (b < B) ? len_of(b) : 0;
+      int nbg;
+      const int4 c = counts(b, L, nbg);
+      const Scan4 sc = block_scan4(c, s_scan);
+      const Scan4 sb = block_scan4(make_int4(nbg, 0, 0, 0), s_scan);
+      if (b < B) {
+        const int4 pre = make_int4(carry.x + sc.incl.x - c.x, carry.y + sc.incl.y - c.y,
+                                   carry.z + sc.incl.z - c.z, carry.w + sc.incl.w - c.w);
+        place(b, L, pre, carry_big + sb.incl.x - nbg);
+      }
+      carry.x += sc.total.x;
+      carry.y += sc.total.y;
+      carry.z += sc.total.z;
+      carry.w += sc.total.w;
+      carry_big += sb.total.x;
+    }
   }
 
   // 4) header
@@ -2183,8 +2248,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     hdr[1] = chunk;
     hdr[2] = any_bad ? MLA_CHECK_SEQ_LEN_RANGE : 0;
     hdr[3] = 0;
-    hdr[4] = 2 * nx * G;  // items placed as XCD-sharing pairs
-    hdr[5] = carry_big * units_per_req;
+    hdr[4] = 2 * nx * (NP / nx);  // items placed as XCD-sharing pairs
+    hdr[5] = NBIG * units_per_req;
     hdr[6] = 0;
   }
 }
