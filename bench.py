@@ -203,11 +203,13 @@ def _cpu_model() -> str:
 
 def stream_read_record(gib: int = 4, reps: int = 5) -> dict:
     """Read-only streaming bandwidth this GPU attains: the probe library's
-    plain 16-byte global loads (mode 0) and direct-to-LDS loads (mode 1, the
-    path the decode kernel stages rows with) over a 4 GiB buffer, 16x the
-    Infinity Cache, with 1, 2 and 4 workgroups of 256 threads per CU; HIP
-    events around `reps` launches of each.  Reports every setting and the best
-    per mode, in decimal GB/s."""
+    plain 16-byte global loads and direct-to-LDS loads (the path the decode
+    kernel stages rows with) over a 4 GiB buffer, 16x the Infinity Cache,
+    with 1, 2 and 4 workgroups of 256 threads per CU; HIP events around `reps`
+    launches of each.  Two access patterns: the whole GPU sweeping the buffer
+    front to back, and every workgroup streaming its own contiguous region
+    (the pattern of the decode's work items, each walking its own blocks).
+    Reports every setting and the best per mode, in decimal GB/s."""
     import ctypes
     import torch
     from mla_latent_cache_absorbed_amd import build as _b
@@ -222,7 +224,8 @@ def stream_read_record(gib: int = 4, reps: int = 5) -> dict:
     sink = torch.empty(lib.mla_probe_sink_bytes(4), dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream()
     runs = {}
-    for mode, name in ((0, "global_load_to_registers"), (1, "direct_to_lds")):
+    for mode, name in ((0, "global_load_to_registers"), (1, "direct_to_lds"),
+                       (2, "own_region_global_load_to_registers"), (3, "own_region_direct_to_lds")):
         for wpc in (1, 2, 4):
             n = lib.mla_probe_stream_read(x.data_ptr(), x.numel(), mode, wpc, sink.data_ptr(),
                                           st.cuda_stream)
@@ -240,7 +243,8 @@ def stream_read_record(gib: int = 4, reps: int = 5) -> dict:
             runs[f"{name}_wg{wpc}"] = n / t / 1e9
     del x, sink
     best = {m: max(v for k, v in runs.items() if k.startswith(m))
-            for m in ("global_load_to_registers", "direct_to_lds")}
+            for m in ("global_load_to_registers", "direct_to_lds",
+                      "own_region_global_load_to_registers", "own_region_direct_to_lds")}
     return {"bytes_per_launch": int(n), "gb_s": runs, "best_gb_s": best,
             "frac_of_peak": {m: v / HBM_PEAK_GBS for m, v in best.items()}}
 
@@ -275,7 +279,7 @@ def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
     cp_gbs = 2 * x.numel() / t_cp / 1e9
     mm_tfs = 2 * 8192 ** 3 / t_mm / 1e12
     del x, y, a, bm
-    read_best = max(sr["best_gb_s"].values())
+    read_best = max(sr["best_gb_s"][m] for m in ("global_load_to_registers", "direct_to_lds"))
     return {"stream_read": sr, "copy_read_write_gbs": cp_gbs, "bf16_gemm_tflops": mm_tfs,
             "attend_frac_of_stream_read": achieved_gbs / read_best,
             "attend_frac_of_copy": achieved_gbs / cp_gbs,

@@ -7,10 +7,15 @@
 //   mode 1  16-byte direct-to-LDS loads, the path the decode kernel stages
 //           latent rows with: each wave keeps eight 1 KB loads in flight into
 //           its own 8 KB of LDS.
+//   modes 2 and 3  as 0 and 1, but each workgroup streams its own contiguous
+//           region of the buffer (bytes / grid) from start to end, the access
+//           pattern of a decode whose work items each walk their own run of
+//           cache blocks; in modes 0 and 1 every workgroup walks the buffer
+//           with a grid stride, so the whole GPU sweeps it front to back
+//           (consecutive workgroups read consecutive 32 KB pieces).
 //
-// Every workgroup walks the buffer with a grid stride, so consecutive
-// workgroups read consecutive 4 KB pieces.  bytes must be a multiple of
-// (grid * 32 KB); the host entry point rounds it down.
+// bytes must be a multiple of (grid * 32 KB); the host entry point rounds it
+// down.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,12 +26,18 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr size_t kStep = size_t(kThreads) * 16 * kUnroll;  // bytes per workgroup iteration
 
+// index of the 32 KB piece a workgroup reads in iteration it
+template <bool kOwnRegion>
+__device__ __forceinline__ size_t piece(size_t it, size_t n_iter) {
+  return kOwnRegion ? size_t(blockIdx.x) * n_iter + it : it * gridDim.x + blockIdx.x;
+}
+
+template <bool kOwnRegion>
 __global__ __launch_bounds__(kThreads) void read_regs(const uint4* __restrict__ p, size_t n_iter,
                                                       uint32_t* __restrict__ sink) {
-  const size_t grid = gridDim.x;
   uint32_t acc = 0;
   for (size_t it = 0; it < n_iter; ++it) {
-    const uint4* base = p + (it * grid + blockIdx.x) * (kStep / 16) + threadIdx.x;
+    const uint4* base = p + piece<kOwnRegion>(it, n_iter) * (kStep / 16) + threadIdx.x;
     uint4 v[kUnroll];
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) v[j] = base[j * kThreads];
@@ -36,16 +47,16 @@ __global__ __launch_bounds__(kThreads) void read_regs(const uint4* __restrict__ 
   sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
 }
 
+template <bool kOwnRegion>
 __global__ __launch_bounds__(kThreads) void read_lds(const char* __restrict__ p, size_t n_iter,
                                                      uint32_t* __restrict__ sink) {
   // 4 waves x 8 KB
   __shared__ __attribute__((aligned(1024))) uint32_t ring[kThreads / 64 * 8 * 256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t grid = gridDim.x;
   uint32_t* mine = ring + w * 8 * 256;
   for (size_t it = 0; it < n_iter; ++it) {
     // the workgroup's 32 KB: wave w takes 1 KB pieces w, w + 4, ...
-    const char* base = p + (it * grid + blockIdx.x) * kStep + size_t(w) * 1024 + lane * 16;
+    const char* base = p + piece<kOwnRegion>(it, n_iter) * kStep + size_t(w) * 1024 + lane * 16;
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j)
       __builtin_amdgcn_global_load_lds(base + j * 4096, mine + j * 256, 16, 0, 0);
@@ -77,7 +88,7 @@ size_t mla_probe_sink_bytes(int32_t wg_per_cu) {
 
 size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_t wg_per_cu,
                              void* sink, void* stream) {
-  if (!buf || !sink || wg_per_cu < 1 || (mode != 0 && mode != 1)) return 0;
+  if (!buf || !sink || wg_per_cu < 1 || mode < 0 || mode > 3) return 0;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -86,12 +97,15 @@ size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_
   const size_t n_iter = bytes / (grid * kStep);
   if (n_iter == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  if (mode == 0)
-    hipLaunchKernelGGL(read_regs, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const uint4*>(buf), n_iter, static_cast<uint32_t*>(sink));
-  else
-    hipLaunchKernelGGL(read_lds, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const char*>(buf), n_iter, static_cast<uint32_t*>(sink));
+  const uint4* p4 = static_cast<const uint4*>(buf);
+  const char* pc = static_cast<const char*>(buf);
+  uint32_t* sk = static_cast<uint32_t*>(sink);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(read_regs<false>, dim3(grid), dim3(kThreads), 0, st, p4, n_iter, sk); break;
+    case 1: hipLaunchKernelGGL(read_lds<false>, dim3(grid), dim3(kThreads), 0, st, pc, n_iter, sk); break;
+    case 2: hipLaunchKernelGGL(read_regs<true>, dim3(grid), dim3(kThreads), 0, st, p4, n_iter, sk); break;
+    default: hipLaunchKernelGGL(read_lds<true>, dim3(grid), dim3(kThreads), 0, st, pc, n_iter, sk); break;
+  }
   if (hipGetLastError() != hipSuccess) return 0;
   return n_iter * grid * kStep;
 }
