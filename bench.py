@@ -10,10 +10,11 @@ Before the warm-up steps, untimed steps run for --prewarm-ms (250 ms): from
 idle the GPU's clock needs ~35 ms of load to settle, and steps in that
 window take up to twice as long.
 
-Prints one JSON line with the metric (cached-token reads/s), a roofline
-record for the attend kernel (HIP events around every attend launch on the
-stream it runs on), and the CPU oracle timed on a bounded sample of the same
-workload on the host cores.
+Prints one JSON line with the metric (cached-token reads/s, from the timed
+steps between two events), a roofline record for the attend kernel (from a
+second run of as many steps with HIP events around every attend launch on
+the stream it runs on), and the CPU oracle timed on a bounded sample of the
+same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload dp_rank]
 """
@@ -393,9 +394,10 @@ def absorb_record(B: int, H: int, reps: int = 100, prewarm_ms: float = 0.0) -> d
 
 def fp8_record(w, layers_copies: int, steps: int, warmup: int, prewarm_ms: float = 0.0) -> dict:
     """The same decode step over an FP8 (e4m3) copy of the workload's cache:
-    fresh fp8 caches rotated like the bf16 ones, plan + attend per step, HIP
-    events around every attend launch, after the same pre-warm as the bf16
-    steps (building the fp8 caches leaves the GPU idle for a while)."""
+    fresh fp8 caches rotated like the bf16 ones, plan + attend per step, after
+    the same pre-warm as the bf16 steps (building the fp8 caches leaves the
+    GPU idle for a while); the steps are timed between two events, then a
+    second run brackets every attend launch with HIP events."""
     import torch
     import mla_latent_cache_absorbed_amd as mla
     from mla_latent_cache_absorbed_amd import accounting as acc
@@ -425,16 +427,22 @@ def fp8_record(w, layers_copies: int, steps: int, warmup: int, prewarm_ms: float
     for i in range(warmup):
         step(n_pre + i)
     torch.cuda.synchronize()
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    n0 = n_pre + warmup
     start.record()
     for i in range(steps):
-        step(n_pre + warmup + i, pairs[i])
+        step(n0 + i)
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / steps
+    # the attend launches on their own, in a second run (each event record
+    # adds a few microseconds between launches)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for i in range(steps):
+        step(n0 + steps + i, pairs[i])
+    torch.cuda.synchronize()
     att = sorted(a.elapsed_time(b) for a, b in pairs)
     att_avg = sum(att) / len(att)
     seq = w.seq_lens_list()
@@ -489,8 +497,10 @@ def measure(wls, steps: int, warmup: int, prewarm_ms: float) -> dict:
     """Timed decode steps over the workload: one step is one plan and one
     attend per layer (step61: 61 layers, each on its own cache), all on the
     current stream.  Untimed steps for prewarm_ms, then `warmup` steps, then
-    `steps` steps between two events; HIP events also bracket every attend
-    launch (on the stream the kernel runs on)."""
+    `steps` steps between two events: the step time.  A second run of `steps`
+    steps brackets every attend launch with HIP events (on the stream the
+    kernel runs on) for the kernel's own duration; it is kept out of the
+    first, since each event record adds a few microseconds between launches."""
     import torch
     import mla_latent_cache_absorbed_amd as mla
     from mla_latent_cache_absorbed_amd import workloads as wl
@@ -526,20 +536,26 @@ def measure(wls, steps: int, warmup: int, prewarm_ms: float) -> dict:
         step(n_pre + i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    n0 = n_pre + warmup
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(n0 + i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    # the attend launches on their own
     n_attend = steps * layers
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_attend)]
     pairs = [(evs[2 * j], evs[2 * j + 1]) for j in range(n_attend)]
     queue = [e for p in pairs for e in p]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
     for i in range(steps):
-        step(n_pre + warmup + i, queue)
-    stop.record(stream)
+        step(n0 + steps + i, queue)
     torch.cuda.synchronize()
     attend_ms = sorted(a.elapsed_time(b) for a, b in pairs)
-    return {"layers": layers, "ms_step": start.elapsed_time(stop) / steps, "fp8": fp8,
+    return {"layers": layers, "ms_step": ms_step, "fp8": fp8,
             "attend_avg_ms": sum(attend_ms) / len(attend_ms),
             "attend_median_ms": attend_ms[len(attend_ms) // 2], "attend_min_ms": attend_ms[0],
             "hdr": ws.header(), "prewarm_steps": n_pre}
