@@ -87,8 +87,8 @@ typedef enum {
 /* Bytes of workspace needed for a batch of B requests with H heads, a block
  * table of M entries per request and block size BS.  Returns 0 when the sizes
  * are outside the supported set.  The figure covers the work plan, two
- * counters per request and fp32 split-KV partials for at most B + 1024 work
- * items. */
+ * counters per request and split-KV partials (fp32; bf16 halves for
+ * requests split in two) for at most B + 1024 work items. */
 size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS);
 
 /* Whole decode: the plan call followed by the attend call below.  The chunk
@@ -101,8 +101,13 @@ mla_status mla_decode(const void* q, const void* latent_cache,
 
 /* Step 1 — split-KV work plan.  One small kernel reads seq_lens and writes
  * into the workspace a list of work items (request, token range), each at
- * most chunk_tokens long: full chunks first, then each request's shorter last
- * chunk, then one item per empty request.  chunk_tokens = 0 lets the device
+ * most chunk_tokens long: first the items of requests split into exactly two
+ * (pairs; the two items of pair j sit nx positions apart for the first
+ * nx * floor(pairs / nx) pairs, nx being the GPU's XCD count for 33 or more
+ * heads and 1 otherwise, so that workgroups on one XCD take both, and side
+ * by side after them), then the full chunks of every other request, then
+ * their shorter last chunks, then one item per empty request.
+ * chunk_tokens = 0 lets the device
  * pick the chunk (a multiple of 32 tokens) that minimises an estimate of the
  * makespan on this GPU's compute units; a positive value forces that chunk
  * size (it must be a multiple of 32, and B * ceil(M*BS / chunk_tokens) must
@@ -112,13 +117,16 @@ mla_status mla_decode(const void* q, const void* latent_cache,
  * Workspace layout written by the plan (int32 words unless noted):
  *   [0] number of work items   [1] chunk tokens   [2] data-check bits
  *   [3] work-queue counter (0 after the plan and after every attend call)
- *   [4] number of full items   [5] number of merge units (16 per request
- *   split into 3 or more items)   [6] merge-unit queue counter (0 between
- *   calls)
- *   at byte 256: per request 4 words (first full item, full-item count,
- *   remainder item or -1, total item count); then, 256-byte aligned, two
- *   counters per request (tickets taken, partials published; 0 between
- *   calls); then the list of requests split into 3 or more items; then per
+ *   [4] number of items placed as XCD-sharing pairs (2 nx floor(pairs/nx))
+ *   [5] number of merge units (16 per request split into 3 or more items
+ *   with 65 or more heads, 8 with 33 to 64, 4 with 32 or fewer)
+ *   [6] merge-unit queue counter (0 between calls)
+ *   at byte 256: per request 4 words: for a pair (position of its first
+ *   item, 1, position of its second item, 2), otherwise (first full item,
+ *   full-item count, remainder item or -1, total item count); then,
+ *   256-byte aligned, two counters per request (a pair with 33 or more
+ *   heads: each item's publish word; otherwise tickets taken, partials
+ *   published; 0 between calls); then the list of requests split into 3 or more items; then per
  *   item 4 words (request, first token, end token, the request's item
  *   count). */
 mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
@@ -128,13 +136,17 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
 /* Step 2 — attention over every work item of the plan (the hot kernel), and
  * the split-KV merge.  An item that covers a whole request writes out/lse
  * directly; an empty request gets out = 0, lse = -inf.  When a request is
- * split, its items write their normalised fp32 outputs and log-sum-exps into
- * the workspace and they are merged, summing in item order:
- * lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) * o_s (bf16, RNE).
- * A request split in two is merged by whichever of its items finishes last
- * (that item does not write its own partial); wider splits are merged in 16
- * column blocks by whichever workgroups are free once every item has been
- * taken.  The result does not depend on which workgroup merges or when.
+ * split, its items' normalised outputs and log-sum-exps are merged, summing
+ * in item order: lse = ln sum_s exp(lse_s), out = sum_s exp(lse_s - lse) *
+ * o_s (bf16, RNE).  With 33 or more heads the two items of a request split
+ * in two each merge half of its heads: each publishes, in the workspace,
+ * its bf16 partial of the heads the other item merges (with its
+ * log-sum-exps), sets its publish word, waits for the other's, and
+ * combines; with 32 or fewer heads the item that finishes second merges
+ * the other's fp32 partial.  Wider splits write fp32 partials and are
+ * merged in column blocks by whichever workgroups are free once every item
+ * has been taken.  The result does not depend on which
+ * workgroup merges or when.
  * Needs a plan made with the same B, H, M, BS. */
 mla_status mla_decode_attend(const void* q, const void* latent_cache,
                              const int32_t* block_table, float scale,
