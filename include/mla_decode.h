@@ -69,7 +69,11 @@ typedef enum {
                                rounded to fp32, overflows                         */
   MLA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required         */
   MLA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed         */
-  MLA_ERR_ALIGNMENT = 7     /* a pointer violates the alignment stated above      */
+  MLA_ERR_ALIGNMENT = 7,    /* a pointer violates the alignment stated above      */
+  /* Not statuses: they widen the type's range to every int32 value, so that
+   * any value a caller passes to mla_status_string is a valid mla_status. */
+  MLA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  MLA_STATUS_RANGE_MAX_ = 2147483647
 } mla_status;
 
 /* Bits of the data-check word raised in the workspace (see mla_decode_read_error). */

@@ -13,6 +13,16 @@ LIB = os.path.join(HERE, "libmla_decode.so")
 # read-bandwidth probes for the benchmark (not part of the decode path)
 PROBE_SRC = os.path.join(HERE, "csrc", "hbm_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
+# the same library with AddressSanitizer and UndefinedBehaviorSanitizer in
+# its host code only (the GPU code is built as usual), for the host-side
+# tests; loaded with the sanitizer runtime preloaded
+HOSTSAN_LIB = os.path.join(HERE, "libmla_decode_hostsan.so")
+HOSTSAN_FLAGS = [
+    "-O1", "-g",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -57,6 +67,29 @@ def build(verbose: bool = False, extra=()) -> str:
     if probs:
         raise RuntimeError("MFMA operand hazards in the compiled code:\n" + "\n".join(probs))
     return LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too), or "" if it is not installed."""
+    import glob
+    llvm = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "llvm")
+    for pat in ("lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so",
+                "lib/clang/*/lib/x86_64-unknown-linux-gnu/libclang_rt.asan.so"):
+        hits = sorted(glob.glob(os.path.join(llvm, pat)))
+        if hits:
+            return hits[-1]
+    return ""
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Compile ``libmla_decode_hostsan.so`` unless it is newer than every
+    source and header; returns its path."""
+    deps = SOURCES + [os.path.join(ROOT, "include", h) for h in os.listdir(os.path.join(ROOT, "include"))]
+    if os.path.exists(HOSTSAN_LIB) and os.path.getmtime(HOSTSAN_LIB) > max(map(os.path.getmtime, deps)):
+        return HOSTSAN_LIB
+    _compile(SOURCES, HOSTSAN_LIB, verbose, HOSTSAN_FLAGS)
+    return HOSTSAN_LIB
 
 
 if __name__ == "__main__":
