@@ -2648,6 +2648,7 @@ const char* mla_status_string(mla_status s) {
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
     case MLA_ERR_HIP: return "MLA_ERR_HIP";
     case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+    default: break;  // the range sentinels and any other value
   }
   return "MLA_ERR_UNKNOWN";
 }
