@@ -72,7 +72,9 @@ constexpr int kRowB = kKC * 2;           // bytes per LDS row
 
 __device__ __forceinline__ int lds_slot(int row, int c16) { return row * kRowB + 16 * (c16 ^ (row & 15)); }
 
-template <int K, int NT>
+// kWStream: W is read with non-temporal loads (it streams through the
+// caches; a gain for the absorption, a loss for the up-projection, measured)
+template <int K, int NT, bool kWStream>
 __global__ __launch_bounds__(256, 2) void mla_head_gemm_kernel(GemmArgs a) {
   static_assert(K % kKC == 0, "K is a multiple of the chunk");
   constexpr int kWRows = 32 * NT;
@@ -102,20 +104,24 @@ __global__ __launch_bounds__(256, 2) void mla_head_gemm_kernel(GemmArgs a) {
 
   for (int kc = 0; kc < K; kc += kKC) {
     // stage: row q < kWRows is W row n0 + q, else X row bbase + q - kWRows
-    // (rows past B load row B - 1; their results are never stored)
+    // (rows past B load row B - 1; their results are never stored).  Load j
+    // covers rows 16 j .. 16 j + 15, so whether it reads W or X is known at
+    // compile time.
+    static_assert(kWRows % 16 == 0, "W rows fill whole loads");
+    constexpr int kWLoads = kWRows / 16;
+    const int c16 = tid & 15;
     i32x4 v[kLoads];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c >> 4, c16 = c & 15;
-      const __bf16* src;
-      if (row < kWRows) {
-        src = a.W + ((long long)h * a.N + n0 + row) * K + kc + 8 * c16;
-      } else {
-        const int b = min(bbase + row - kWRows, a.B - 1);
-        src = a.X + (long long)b * a.x_row + (long long)h * a.x_head + kc + 8 * c16;
-      }
-      v[j] = *reinterpret_cast<const i32x4*>(src);
+    for (int j = 0; j < kWLoads; ++j) {
+      const int row = (tid >> 4) + 16 * j;
+      const i32x4* src = reinterpret_cast<const i32x4*>(a.W + ((long long)h * a.N + n0 + row) * K + kc + 8 * c16);
+      if constexpr (kWStream) v[j] = __builtin_nontemporal_load(src);
+      else v[j] = *src;
+    }
+#pragma unroll
+    for (int j = kWLoads; j < kLoads; ++j) {
+      const int b = min(bbase + (tid >> 4) + 16 * j - kWRows, a.B - 1);
+      v[j] = *reinterpret_cast<const i32x4*>(a.X + (long long)b * a.x_row + (long long)h * a.x_head + kc + 8 * c16);
     }
     if (kc > 0) __syncthreads();  // the previous chunk's fragment reads are done
 #pragma unroll
@@ -166,9 +172,12 @@ __global__ __launch_bounds__(256, 2) void mla_head_gemm_kernel(GemmArgs a) {
     const int idx = tid + 256 * j;
     const int q = idx / kChunks, c = idx % kChunks;
     const int b = bbase + q;
+    // the output is written once and read by the next kernel: it streams
+    // out (non-temporal stores)
     if (b < a.B)
-      *reinterpret_cast<i32x4*>(a.Y + (long long)b * a.y_row + (long long)h * a.y_head + n0 + 8 * c) =
-          *reinterpret_cast<const i32x4*>(lds + out_slot(q, c));
+      __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(lds + out_slot(q, c)),
+                                  reinterpret_cast<i32x4*>(a.Y + (long long)b * a.y_row +
+                                                           (long long)h * a.y_head + n0 + 8 * c));
   }
   // the RoPE part rides along with group 0: 32 rows x 128 B per wave
   if (a.R != nullptr && ng == 0) {
@@ -217,12 +226,12 @@ mla_status check_bh(int32_t B, int32_t H) {
   return MLA_OK;
 }
 
-template <int K, int NT>
+template <int K, int NT, bool kWStream>
 mla_status launch_gemm(const GemmArgs& a, void* stream) {
   const int T = a.N / (32 * NT);
   const int groups = (a.H + 7) / 8;
   dim3 grid(8 * T * groups, (a.B + 127) / 128);
-  hipLaunchKernelGGL((mla_head_gemm_kernel<K, NT>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL((mla_head_gemm_kernel<K, NT, kWStream>), grid, dim3(256), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -261,7 +270,7 @@ mla_status mla_absorb_query(const void* q_in, const void* w_uk_t, void* q, int32
   a.R = static_cast<const __bf16*>(q_in) + kDN;
   a.r_row = (long long)H * kDQ;
   a.r_head = kDQ;
-  return launch_gemm<kDN, 4>(a, stream);
+  return launch_gemm<kDN, 4, true>(a, stream);
 }
 
 mla_status mla_up_project(const void* out, const void* w_uv, void* o, int32_t B, int32_t H,
@@ -284,7 +293,7 @@ mla_status mla_up_project(const void* out, const void* w_uv, void* o, int32_t B,
   a.R = nullptr;
   a.r_row = 0;
   a.r_head = 0;
-  return launch_gemm<kDV, 1>(a, stream);
+  return launch_gemm<kDV, 1, false>(a, stream);
 }
 
 }  // extern "C"
