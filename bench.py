@@ -353,9 +353,10 @@ def absorb_record(B: int, H: int, reps: int = 96, prewarm_ms: float = 0.0, copie
     HIP events around `reps` launches of each, rotating over `copies`
     independent sets of weights and activations (~80 MB each, together well
     past the 256 MB Infinity Cache), as the layers of a model do; bytes are
-    the weights plus the activations read and written once.  The time with
-    the same inputs every launch (then served from the Infinity Cache) is
-    reported beside it."""
+    the weights plus the activations read and written once.  Reported beside
+    it: the time with only the weights rotating (the activations fixed, as
+    they are when the kernel before has just written them) and with the same
+    inputs every launch (then served from the Infinity Cache)."""
     import torch
     import mla_latent_cache_absorbed_amd as mla
     dev = torch.device("cuda")
@@ -371,38 +372,44 @@ def absorb_record(B: int, H: int, reps: int = 96, prewarm_ms: float = 0.0, copie
         sets.append((q_in, w_uk_t, w_uv, out, torch.empty((B, H, 576), dtype=torch.bfloat16, device=dev),
                      torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)))
 
-    def timed(fn, rotate):
-        fn(0)
-        prewarm(lambda i: fn(i % copies if rotate else 0), prewarm_ms)
+    # which set's activations and which set's weights launch i uses
+    modes = {"all": lambda i: (i % copies, i % copies), "weights": lambda i: (0, i % copies),
+             "none": lambda i: (0, 0)}
+
+    def timed(fn, mode):
+        pick = modes[mode]
+        fn(0, 0)
+        prewarm(lambda i: fn(*pick(i)), prewarm_ms)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
-            fn(i % copies if rotate else 0)
+            fn(*pick(i))
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps * 1e-3
 
-    def absorb(i):
-        q_in, w_uk_t, _, _, q, _ = sets[i]
-        mla.absorb_query(q_in, w_uk_t, q)
+    def absorb(i, j):
+        mla.absorb_query(sets[i][0], sets[j][1], sets[i][4])
 
-    def up(i):
-        _, _, w_uv, out, _, o = sets[i]
-        mla.up_project(out, w_uv, o)
+    def up(i, j):
+        mla.up_project(sets[i][3], sets[j][2], sets[i][5])
 
     flops = 2.0 * B * H * 128 * 512
     res = {}
     for name, fn, nbytes in [
             ("absorb_query", absorb, H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 576 * 2),
             ("up_project", up, H * 128 * 512 * 2 + B * H * 512 * 2 + B * H * 128 * 2)]:
-        t = timed(fn, True)
-        t_same = timed(fn, False)
+        t = timed(fn, "all")
+        t_w = timed(fn, "weights")
+        t_same = timed(fn, "none")
         gbs = nbytes / t / 1e9
         res[name] = {"kernel": "mla_head_gemm_kernel", "launch_us": t * 1e6,
                      "algorithmic_bytes": nbytes, "gb_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                      "tflops": flops / t / 1e12, "copies_rotated": copies,
+                     "launch_us_weights_rotating": t_w * 1e6,
+                     "hbm_frac_weights_rotating": nbytes / t_w / 1e9 / HBM_PEAK_GBS,
                      "launch_us_same_inputs": t_same * 1e6}
     del sets
     return res
