@@ -58,6 +58,10 @@ def parse():
                         "from idle the GPU clock takes ~35 ms of load to settle")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the fp8, append, absorption and attainable-peak records")
+    p.add_argument("--trace-summary", default=None,
+                   help="write profiles/bench_default_run_kernel_trace.md from the rocprofv3 "
+                        "--kernel-trace --stats output under this directory (the default run), "
+                        "then exit (no GPU needed)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
     p.add_argument("--profile-dir", default=None,
@@ -712,8 +716,39 @@ def write_profiles(name: str, d: str) -> None:
         fh.write("\n".join(lines) + "\n")
 
 
+TRACE_ALL_CMD = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 400 rocprofv3 --kernel-trace --stats "
+                 "-d $O/kt_all -o kt --output-format csv -- python -u $R/bench.py --no-cpu")
+
+
+def write_trace_summary(d: str) -> str:
+    """profiles/bench_default_run_kernel_trace.md: every kernel of the default
+    bench run (all workloads and the fp8, append, absorption and probe
+    records), from rocprofv3's kernel statistics under d."""
+    stats = _rocprof_rows(d, "kernel_stats.csv")
+    lines = ["# Kernel trace of the default benchmark run", "",
+             "Command, on one MI355X, with `R` the repository root and `O` an output directory:", "",
+             "```", TRACE_ALL_CMD, "```", "",
+             f"Source hash (sha256, first 16 hex of mla_decode.hip): `{src_hash()}`", "",
+             "Every kernel the run launches: the timed steps of each workload and the records after "
+             "them (plan, attend, fp8 attend, append, absorption GEMMs, probes) and the input "
+             "generation (torch kernels).", "",
+             "| kernel | calls | average ns | min ns | max ns | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        nm = r.get("Name", r.get("KernelName", ""))
+        short = nm if len(nm) < 90 else nm[:87] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                     f"{float(r['MaxNs']):.0f} | {float(r['Percentage']):.2f} |")
+    out = os.path.join(PROFILES, "bench_default_run_kernel_trace.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return out
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        print(write_trace_summary(args.trace_summary))
+        return
     if args.profile_dir:
         write_profiles(args.workload, args.profile_dir)
         return
