@@ -71,3 +71,41 @@ def test_noalloc_full_size_dp_rank_sampled():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.isfinite(o1.float()).all() and torch.isfinite(l1).all()
     _say("[noalloc] dp_rank: bit-identical to mla_decode")
+
+
+@pytest.mark.parametrize("H", [128, 16])
+def test_noalloc_under_graph_capture(H):
+    """The callers this entry point is for include code under HIP graph
+    capture: one call captured (after a warm-up call outside the capture,
+    which takes the scratch array's address), replayed four times with new
+    query values, with an eager no-alloc call on another batch between the
+    replays (it rewrites the shared scratch); every replay is bit-identical
+    to mla_decode on the same values."""
+    w = _gpu(wl.make_custom([2500, 9, 700, 64, 4100], H=H, BS=64, seed=71, poison_unused=True))
+    other = _gpu(wl.make_custom([1500, 3, 333], H=H, BS=16, seed=72))
+    q_in = w.q.clone()
+    out = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mla.decode_noalloc(q_in, w.cache, w.block_table, w.seq_lens, w.scale, out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mla.decode_noalloc(q_in, w.cache, w.block_table, w.seq_lens, w.scale, out, lse)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda")
+    for rep in range(4):
+        gen.manual_seed(200 + rep)
+        q_new = torch.randn(w.q.shape, generator=gen, device="cuda").to(torch.bfloat16)
+        q_in.copy_(q_new)
+        _noalloc(other)  # eager use of the same scratch between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, l_e = mla.decode(q_new, w.cache, w.block_table, w.seq_lens, w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_e) and torch.equal(lse, l_e), rep
+    _say(f"[noalloc] graph capture H={H}: 4 replays bit-identical to mla_decode")
