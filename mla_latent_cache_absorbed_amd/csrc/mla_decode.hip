@@ -1983,6 +1983,9 @@ __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long x)
 struct Scan4 {
   int4 incl, total;
 };
+// kReuse: s_scan is written again after this scan, so every wave must have
+// read it first (a second barrier).
+template <bool kReuse = true>
 __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -2007,13 +2010,14 @@ __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
   Scan4 r;
   r.incl = make_int4(x.x + pre.x, x.y + pre.y, x.z + pre.z, x.w + pre.w);
   r.total = tot;
-  __syncthreads();  // every wave has read s_scan before the next scan writes it
+  if (kReuse) __syncthreads();  // every wave has read s_scan before the next scan writes it
   return r;
 }
 
-// Items are laid out full chunks first, then the last (shorter) chunk of each
-// request, then one item per empty request.  With at most kPlanLens requests
-// the (clamped) lengths are read from memory once and kept in LDS.
+// Items are laid out as the pairs (requests split into exactly two items)
+// first, then the full chunks of every other request, then their last
+// (shorter) chunks, then one item per empty request.  With at most kPlanLens
+// requests the (clamped) lengths are read from memory once and kept in LDS.
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
     int ovh, int cap, int units_per_req, int nx, int32_t* __restrict__ hdr, int4* __restrict__ req,
@@ -2147,8 +2151,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   // Writes request b's record, its items and its merge-unit entry, given
   // the exclusive prefix counts of the requests before it (full chunks,
   // remainders, empties, pairs and widely split requests of the others).
-  auto place = [&](int b, int L, int4 pre, int pre_big) {
-    const int nf0 = L / chunk, nr0 = (L % chunk) ? 1 : 0;
+  auto place = [&](int b, int L, int nf0, int nr0, int4 pre, int pre_big) {
     const int cnt = nf0 + nr0;
     const int Q0 = 2 * NP;  // first position of the other items
     if (cnt == 2) {
@@ -2171,8 +2174,9 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   };
   // this request's counts (full chunks, remainders, empty, pair) and
   // whether it is split widely enough for the merge units
-  auto counts = [&](int b, int L, int& nbg) {
-    const int nf0 = L / chunk, nr0 = (L % chunk) ? 1 : 0;
+  auto counts = [&](int b, int L, int& nbg, int& nf0, int& nr0) {
+    nf0 = L / chunk;
+    nr0 = (L - nf0 * chunk) ? 1 : 0;
     const bool pair = b < B && nf0 + nr0 == 2;
     nbg = (b < B && nf0 + nr0 >= kMergeMinItems) ? 1 : 0;
     return make_int4(pair ? 0 : nf0, pair ? 0 : nr0, (b < B && L == 0) ? 1 : 0, pair ? 1 : 0);
@@ -2185,10 +2189,10 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     //    count and the range-check bits.
     const int b = tid;
     const int L = (b < B) ? s_len[b] : 0;
-    int nbg;
-    const int4 c = counts(b, L, nbg);
+    int nbg, nf0, nr0;
+    const int4 c = counts(b, L, nbg, nf0, nr0);
     const int4 packed = make_int4(c.x, c.y, c.z | (nbg << 16), c.w | ((b < B && bad) ? 1 << 16 : 0));
-    const Scan4 sc = block_scan4(packed, s_scan);
+    const Scan4 sc = block_scan4<false>(packed, s_scan);
     NF = sc.total.x;
     NR = sc.total.y;
     NE = sc.total.z & 0xffff;
@@ -2198,7 +2202,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     if (b < B) {
       const int4 pre = make_int4(sc.incl.x - c.x, sc.incl.y - c.y, (sc.incl.z & 0xffff) - c.z,
                                  (sc.incl.w & 0xffff) - c.w);
-      place(b, L, pre, (sc.incl.z >> 16) - nbg);
+      place(b, L, nf0, nr0, pre, (sc.incl.z >> 16) - nbg);
     }
   } else {
     // 2) totals: the items of pairs and of all other requests, empty
@@ -2206,8 +2210,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     int4 loc = make_int4(0, 0, 0, 0);
     int locbig = 0;
     for (int b = tid; b < B; b += kPlanThreads) {
-      int nbg;
-      const int4 c = counts(b, len_of(b), nbg);
+      int nbg, nf0, nr0;
+      const int4 c = counts(b, len_of(b), nbg, nf0, nr0);
       loc.x += c.x;
       loc.y += c.y;
       loc.z += c.z;
@@ -2228,14 +2232,14 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     for (int b0 = 0; b0 < B; b0 += kPlanThreads) {
       const int b = b0 + tid;
       const int L = (b < B) ? len_of(b) : 0;
-      int nbg;
-      const int4 c = counts(b, L, nbg);
+      int nbg, nf0, nr0;
+      const int4 c = counts(b, L, nbg, nf0, nr0);
       const Scan4 sc = block_scan4(c, s_scan);
       const Scan4 sb = block_scan4(make_int4(nbg, 0, 0, 0), s_scan);
       if (b < B) {
         const int4 pre = make_int4(carry.x + sc.incl.x - c.x, carry.y + sc.incl.y - c.y,
                                    carry.z + sc.incl.z - c.z, carry.w + sc.incl.w - c.w);
-        place(b, L, pre, carry_big + sb.incl.x - nbg);
+        place(b, L, nf0, nr0, pre, carry_big + sb.incl.x - nbg);
       }
       carry.x += sc.total.x;
       carry.y += sc.total.y;
