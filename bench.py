@@ -254,13 +254,55 @@ def stream_read_record(gib: int = 4, reps: int = 5) -> dict:
             "frac_of_peak": {m: v / HBM_PEAK_GBS for m, v in best.items()}}
 
 
+def mfma_loop_record(iters: int = 20000, reps: int = 5) -> dict:
+    """bf16 MFMA rate this GPU attains: the probe library's loop of
+    independent v_mfma_f32_32x32x16_bf16 on random operands, with 1 and 2
+    workgroups of 4 waves per CU (one or two waves per SIMD), HIP events
+    around `reps` launches of each; TFLOP/s and the fraction of the 2.5
+    PFLOP/s dense bf16 peak."""
+    import ctypes
+    import torch
+    from mla_latent_cache_absorbed_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.mla_probe_mfma.restype = ctypes.c_double
+    lib.mla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.mla_probe_sink_bytes.restype = ctypes.c_size_t
+    lib.mla_probe_sink_bytes.argtypes = [ctypes.c_int32]
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    # 4 operand fragments of 64 lanes x 8 bf16, as the kernel indexes them
+    ab = torch.randn(4 * 64 * 8, generator=g, device=dev).to(torch.bfloat16).contiguous()
+    sink = torch.empty(lib.mla_probe_sink_bytes(2), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    runs = {}
+    for wpc in (1, 2):
+        fl = lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(), st.cuda_stream)
+        if fl <= 0:
+            raise RuntimeError("MFMA probe failed to launch")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(), st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        runs[f"wg{wpc}"] = fl / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    del ab, sink
+    best = max(runs.values())
+    return {"tflops": runs, "best_tflops": best, "frac_of_peak": best / MFMA_BF16_PEAK_TFS}
+
+
 def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
     """Peaks this box attains, timed with events: the read-only streaming
-    probes (see stream_read_record), a device-to-device copy of 2 GiB (reads
-    and writes counted) and a bf16 GEMM (8192^3 on hipBLASLt).  The attend
-    kernel's rates are also given as fractions of them."""
+    probes (see stream_read_record), the MFMA loop (see mfma_loop_record), a
+    device-to-device copy of 2 GiB (reads and writes counted) and a bf16 GEMM
+    (8192^3 on hipBLASLt).  The attend kernel's rates are also given as
+    fractions of them."""
     import torch
     sr = stream_read_record()
+    mf = mfma_loop_record()
     dev = torch.device("cuda")
     x = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
@@ -285,9 +327,10 @@ def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:
     mm_tfs = 2 * 8192 ** 3 / t_mm / 1e12
     del x, y, a, bm
     read_best = max(sr["best_gb_s"][m] for m in ("global_load_to_registers", "direct_to_lds"))
-    return {"stream_read": sr, "copy_read_write_gbs": cp_gbs, "bf16_gemm_tflops": mm_tfs,
+    return {"stream_read": sr, "mfma_loop": mf, "copy_read_write_gbs": cp_gbs, "bf16_gemm_tflops": mm_tfs,
             "attend_frac_of_stream_read": achieved_gbs / read_best,
             "attend_frac_of_copy": achieved_gbs / cp_gbs,
+            "attend_frac_of_mfma_loop": tflops / mf["best_tflops"],
             "attend_frac_of_gemm": tflops / mm_tfs}
 
 

@@ -1,6 +1,8 @@
 // Read-only streaming probes of HBM bandwidth on gfx950, used by the
 // benchmark to state the read bandwidth this GPU attains next to its 8 TB/s
-// peak.  Not part of the decode path: built as its own small library.
+// peak, and an MFMA loop that states the bf16 matrix rate it attains next to
+// its 2.5 PFLOP/s peak.  Not part of the decode path: built as its own small
+// library.
 //
 //   mode 0  plain 16-byte global loads into registers, eight in flight per
 //           lane, folded with xor into one word per lane (written once);
@@ -69,6 +71,39 @@ __global__ __launch_bounds__(kThreads) void read_lds(const char* __restrict__ p,
   sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
 }
 
+// MFMA loop: every wave runs `iters` rounds of 2 kChains
+// v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 bf16 products into fp32, 32,768
+// flop each) into kChains independent accumulators, on operands loaded once
+// from `ab` (random bf16, so the products toggle like real data): two A
+// fragments, and the two B fragments in turn; one word per lane goes to the
+// sink so that nothing is optimised away.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kChains = 4;
+
+__global__ __launch_bounds__(kThreads) void mfma_loop(const bf16x8* __restrict__ ab, int iters,
+                                                     float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const bf16x8 a0 = ab[lane], a1 = ab[64 + lane], b0 = ab[128 + lane], b1 = ab[192 + lane];
+  f32x16 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((c & 1) ? a1 : a0, b0, acc[c], 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((c & 1) ? a1 : a0, b1, acc[c], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +143,24 @@ size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_
   }
   if (hipGetLastError() != hipSuccess) return 0;
   return n_iter * grid * kStep;
+}
+
+// Runs the MFMA loop with `wg_per_cu` workgroups of 256 threads (4 waves)
+// per compute unit, `iters` rounds each, on `stream`.  `ab` is a device
+// buffer of at least 256 x 16 bytes of bf16 operands; `sink` as for the
+// stream probe.  Returns the flops of the launch, or 0 on a bad argument or
+// launch failure.
+double mla_probe_mfma(const void* ab, int32_t iters, int32_t wg_per_cu, void* sink, void* stream) {
+  if (!ab || !sink || iters < 1 || wg_per_cu < 1) return 0.0;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0.0;
+  const size_t grid = size_t(ncu) * wg_per_cu;
+  hipLaunchKernelGGL(mfma_loop, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     static_cast<const bf16x8*>(ab), iters, static_cast<float*>(sink));
+  if (hipGetLastError() != hipSuccess) return 0.0;
+  return double(grid) * (kThreads / 64) * double(iters) * 2 * kChains * 32768.0;
 }
 
 }  // extern "C"
