@@ -266,7 +266,7 @@ def mfma_loop_record(iters: int = 20000, reps: int = 5) -> dict:
     lib = ctypes.CDLL(_b.PROBE_LIB)
     lib.mla_probe_mfma.restype = ctypes.c_double
     lib.mla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                   ctypes.c_void_p]
+                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.mla_probe_sink_bytes.restype = ctypes.c_size_t
     lib.mla_probe_sink_bytes.argtypes = [ctypes.c_int32]
     dev = torch.device("cuda")
@@ -275,23 +275,31 @@ def mfma_loop_record(iters: int = 20000, reps: int = 5) -> dict:
     # 4 operand fragments of 64 lanes x 8 bf16, as the kernel indexes them
     ab = torch.randn(4 * 64 * 8, generator=g, device=dev).to(torch.bfloat16).contiguous()
     sink = torch.empty(lib.mla_probe_sink_bytes(2), dtype=torch.uint8, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
     st = torch.cuda.current_stream()
-    runs = {}
+    runs, ghz, busy = {}, {}, {}
     for wpc in (1, 2):
-        fl = lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(), st.cuda_stream)
+        fl = lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(), None, st.cuda_stream)
         if fl <= 0:
             raise RuntimeError("MFMA probe failed to launch")
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(st)
-        for _ in range(reps):
-            lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(), st.cuda_stream)
+        for r in range(reps):
+            lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(),
+                               clk.data_ptr() if r == reps - 1 else None, st.cuda_stream)
         e1.record(st)
         torch.cuda.synchronize()
         runs[f"wg{wpc}"] = fl / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
-    del ab, sink
+        cyc, ticks = (int(v) for v in clk.tolist())
+        # core clock of the first wave's loop, and the share of its cycles
+        # its MFMA pipe was busy (32 cycles per MFMA, 2 x 4 per round)
+        ghz[f"wg{wpc}"] = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else None
+        busy[f"wg{wpc}"] = wpc * iters * 8 * 32 / cyc if cyc > 0 else None
+    del ab, sink, clk
     best = max(runs.values())
-    return {"tflops": runs, "best_tflops": best, "frac_of_peak": best / MFMA_BF16_PEAK_TFS}
+    return {"tflops": runs, "best_tflops": best, "frac_of_peak": best / MFMA_BF16_PEAK_TFS,
+            "core_clock_ghz": ghz, "simd_mfma_busy": busy}
 
 
 def attainable_peaks(achieved_gbs: float, tflops: float) -> dict:

@@ -18,15 +18,39 @@
 //
 // bytes must be a multiple of (grid * 32 KB); the host entry point rounds it
 // down.
+//
+// Every probe kernel holds 160 KB / (workgroups per CU) of LDS, so that the
+// dispatcher places exactly that many workgroups on each compute unit (with
+// less, it may double some up and leave others idle, and the launch then
+// ends with the busiest unit), as the decode kernel's 160 KB does.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr size_t kStep = size_t(kThreads) * 16 * kUnroll;  // bytes per workgroup iteration
+constexpr int kLdsPerCu = 160 * 1024;                       // gfx950
+
+// LDS words of a workgroup when kWpc of them are to share a compute unit
+template <int kWpc>
+constexpr int occ_words() {
+  return kLdsPerCu / kWpc / 4;
+}
+
+// Keeps a workgroup's occupancy array allocated: every thread passes its
+// value through it (one barrier), and the result goes to the sink.
+template <int kWords>
+__device__ __forceinline__ uint32_t through_lds(uint32_t (&occ)[kWords], uint32_t v) {
+  static_assert(kWords >= kThreads, "occupancy array");
+  occ[kWords - kThreads + threadIdx.x] = v;
+  __syncthreads();
+  return occ[kWords - kThreads + ((threadIdx.x + 1) % kThreads)];
+}
 
 // index of the 32 KB piece a workgroup reads in iteration it
 template <bool kOwnRegion>
@@ -34,9 +58,10 @@ __device__ __forceinline__ size_t piece(size_t it, size_t n_iter) {
   return kOwnRegion ? size_t(blockIdx.x) * n_iter + it : it * gridDim.x + blockIdx.x;
 }
 
-template <bool kOwnRegion>
+template <bool kOwnRegion, int kWpc>
 __global__ __launch_bounds__(kThreads) void read_regs(const uint4* __restrict__ p, size_t n_iter,
                                                       uint32_t* __restrict__ sink) {
+  __shared__ uint32_t occ[occ_words<kWpc>()];
   uint32_t acc = 0;
   for (size_t it = 0; it < n_iter; ++it) {
     const uint4* base = p + piece<kOwnRegion>(it, n_iter) * (kStep / 16) + threadIdx.x;
@@ -46,14 +71,15 @@ __global__ __launch_bounds__(kThreads) void read_regs(const uint4* __restrict__ 
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
-  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
+  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = through_lds(occ, acc);
 }
 
-template <bool kOwnRegion>
+template <bool kOwnRegion, int kWpc>
 __global__ __launch_bounds__(kThreads) void read_lds(const char* __restrict__ p, size_t n_iter,
                                                      uint32_t* __restrict__ sink) {
-  // 4 waves x 8 KB
-  __shared__ __attribute__((aligned(1024))) uint32_t ring[kThreads / 64 * 8 * 256];
+  // 4 waves x 8 KB at the start of the workgroup's occupancy array
+  static_assert(occ_words<kWpc>() >= kThreads / 64 * 8 * 256, "ring fits");
+  __shared__ __attribute__((aligned(1024))) uint32_t ring[occ_words<kWpc>()];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t* mine = ring + w * 8 * 256;
   for (size_t it = 0; it < n_iter; ++it) {
@@ -81,13 +107,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kChains = 4;
 
+template <int kWpc>
 __global__ __launch_bounds__(kThreads) void mfma_loop(const bf16x8* __restrict__ ab, int iters,
-                                                     float* __restrict__ sink) {
+                                                     float* __restrict__ sink, uint64_t* __restrict__ clk) {
+  __shared__ uint32_t occ[occ_words<kWpc>()];
   const int lane = threadIdx.x & 63;
   const bf16x8 a0 = ab[lane], a1 = ab[64 + lane], b0 = ab[128 + lane], b1 = ab[192 + lane];
   f32x16 acc[kChains];
 #pragma unroll
   for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
+  // operands in registers before the clocks start
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
@@ -101,7 +132,15 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(const bf16x8* __restrict__
   for (int c = 0; c < kChains; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[c][r];
-  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = s;
+  // the sum depends on every accumulator, so the clocks below follow the loop
+  sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = __uint_as_float(through_lds(occ, __float_as_uint(s)));
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint64_t c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  // first workgroup, first wave: core cycles and 100 MHz ticks of its loop
+  if (clk && blockIdx.x == 0 && threadIdx.x == 0) {
+    clk[0] = c1 - c0;
+    clk[1] = r1 - r0;
+  }
 }
 
 }  // namespace
@@ -109,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(const bf16x8* __restrict__
 extern "C" {
 
 // Streams `bytes` (rounded down to a whole number of workgroup iterations)
-// of the device buffer `buf` once, with `wg_per_cu` workgroups of 256
+// of the device buffer `buf` once, with `wg_per_cu` (1, 2 or 4) workgroups of 256
 // threads per compute unit, on `stream`.  `sink` is a device buffer of at
 // least mla_probe_sink_bytes(wg_per_cu) bytes.  Returns the bytes streamed,
 // or 0 on a bad argument or launch failure.
@@ -123,7 +162,7 @@ size_t mla_probe_sink_bytes(int32_t wg_per_cu) {
 
 size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_t wg_per_cu,
                              void* sink, void* stream) {
-  if (!buf || !sink || wg_per_cu < 1 || mode < 0 || mode > 3) return 0;
+  if (!buf || !sink || !(wg_per_cu == 1 || wg_per_cu == 2 || wg_per_cu == 4) || mode < 0 || mode > 3) return 0;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -135,30 +174,50 @@ size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_
   const uint4* p4 = static_cast<const uint4*>(buf);
   const char* pc = static_cast<const char*>(buf);
   uint32_t* sk = static_cast<uint32_t*>(sink);
-  switch (mode) {
-    case 0: hipLaunchKernelGGL(read_regs<false>, dim3(grid), dim3(kThreads), 0, st, p4, n_iter, sk); break;
-    case 1: hipLaunchKernelGGL(read_lds<false>, dim3(grid), dim3(kThreads), 0, st, pc, n_iter, sk); break;
-    case 2: hipLaunchKernelGGL(read_regs<true>, dim3(grid), dim3(kThreads), 0, st, p4, n_iter, sk); break;
-    default: hipLaunchKernelGGL(read_lds<true>, dim3(grid), dim3(kThreads), 0, st, pc, n_iter, sk); break;
+  auto launch = [&](auto wpc_c) {
+    constexpr int W = decltype(wpc_c)::value;
+    switch (mode) {
+      case 0: hipLaunchKernelGGL((read_regs<false, W>), dim3(grid), dim3(kThreads), 0, st, p4, n_iter, sk); break;
+      case 1: hipLaunchKernelGGL((read_lds<false, W>), dim3(grid), dim3(kThreads), 0, st, pc, n_iter, sk); break;
+      case 2: hipLaunchKernelGGL((read_regs<true, W>), dim3(grid), dim3(kThreads), 0, st, p4, n_iter, sk); break;
+      default: hipLaunchKernelGGL((read_lds<true, W>), dim3(grid), dim3(kThreads), 0, st, pc, n_iter, sk); break;
+    }
+  };
+  switch (wg_per_cu) {
+    case 1: launch(std::integral_constant<int, 1>{}); break;
+    case 2: launch(std::integral_constant<int, 2>{}); break;
+    default: launch(std::integral_constant<int, 4>{}); break;
   }
   if (hipGetLastError() != hipSuccess) return 0;
   return n_iter * grid * kStep;
 }
 
-// Runs the MFMA loop with `wg_per_cu` workgroups of 256 threads (4 waves)
+// Runs the MFMA loop with `wg_per_cu` (1, 2 or 4) workgroups of 256 threads (4 waves)
 // per compute unit, `iters` rounds each, on `stream`.  `ab` is a device
 // buffer of at least 256 x 16 bytes of bf16 operands; `sink` as for the
-// stream probe.  Returns the flops of the launch, or 0 on a bad argument or
-// launch failure.
-double mla_probe_mfma(const void* ab, int32_t iters, int32_t wg_per_cu, void* sink, void* stream) {
-  if (!ab || !sink || iters < 1 || wg_per_cu < 1) return 0.0;
+// stream probe; `clk`, if not null, a device buffer of two uint64 that gets
+// the core-clock cycles and the 100 MHz real-time ticks of the first wave's
+// loop.  Returns the flops of the launch, or 0 on a bad argument or launch
+// failure.
+double mla_probe_mfma(const void* ab, int32_t iters, int32_t wg_per_cu, void* sink, void* clk,
+                      void* stream) {
+  if (!ab || !sink || iters < 1 || !(wg_per_cu == 1 || wg_per_cu == 2 || wg_per_cu == 4)) return 0.0;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0.0;
   const size_t grid = size_t(ncu) * wg_per_cu;
-  hipLaunchKernelGGL(mfma_loop, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
-                     static_cast<const bf16x8*>(ab), iters, static_cast<float*>(sink));
+  auto launch = [&](auto wpc_c) {
+    constexpr int W = decltype(wpc_c)::value;
+    hipLaunchKernelGGL((mfma_loop<W>), dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                       static_cast<const bf16x8*>(ab), iters, static_cast<float*>(sink),
+                       static_cast<uint64_t*>(clk));
+  };
+  switch (wg_per_cu) {
+    case 1: launch(std::integral_constant<int, 1>{}); break;
+    case 2: launch(std::integral_constant<int, 2>{}); break;
+    default: launch(std::integral_constant<int, 4>{}); break;
+  }
   if (hipGetLastError() != hipSuccess) return 0.0;
   return double(grid) * (kThreads / 64) * double(iters) * 2 * kChains * 32768.0;
 }
