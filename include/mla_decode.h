@@ -91,8 +91,9 @@ typedef enum {
 /* Bytes of workspace needed for a batch of B requests with H heads, a block
  * table of M entries per request and block size BS.  Returns 0 when the sizes
  * are outside the supported set.  The figure covers the work plan, two
- * counters per request and split-KV partials (fp32; bf16 halves for
- * requests split in two) for at most B + 1024 work items. */
+ * counters per request and split-KV partials for at most B + 1024 work
+ * items (normalised outputs in bf16 with 33 or more heads, in fp32 with 32
+ * or fewer; log-sum-exps in fp32). */
 size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t M, int32_t BS);
 
 /* Whole decode: the plan call followed by the attend call below.  The chunk
@@ -147,9 +148,12 @@ mla_status mla_decode_plan(const int32_t* seq_lens, int32_t B, int32_t H,
  * its bf16 partial of the heads the other item merges (with its
  * log-sum-exps), sets its publish word, waits for the other's, and
  * combines; with 32 or fewer heads the item that finishes second merges
- * the other's fp32 partial.  Wider splits write fp32 partials and are
- * merged in column blocks by whichever workgroups are free once every item
- * has been taken.  The result does not depend on which
+ * the other's fp32 partial.  Wider splits write partials (bf16 with 33 or
+ * more heads, fp32 with fewer) and are merged in column blocks by
+ * whichever workgroups are free once every item has been taken.  A bf16
+ * partial adds at most one bf16 rounding of the partial (2^-8 of its
+ * magnitude, which is at most max |V| over the request's tokens) to the
+ * merged output.  The result does not depend on which
  * workgroup merges or when.
  * Needs a plan made with the same B, H, M, BS. */
 mla_status mla_decode_attend(const void* q, const void* latent_cache,

@@ -523,7 +523,7 @@ struct Pick<false, A, B> {
   using T = B;
 };
 
-constexpr int kWaveBytesM = 32 * kDV * 4;  // one wave's share of an item's partial
+constexpr int kWaveBytesM = 32 * kDV * 2;  // one wave's share of an item's bf16 partial (32 heads)
 
 // kOne: the block size is 32 tokens or more, so every stage lies in one block.
 // kF8: the cache is fp8 (e4m3); stages hold fp8 rows, whose operands are
@@ -1074,11 +1074,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       continue;
     }
 
-    // Split request.  An item's partial is HP x 512 fp32 in 1 KB blocks:
-    // block (h, cb, g) at byte (64 h + 4 cb + g) KB holds, in lane l's 16
-    // bytes, columns 32 cb + 8 g + 4 (l / 32) .. +3 of head 32 h + l % 32:
-    // the accumulator layout, so that each store instruction writes 1 KB
-    // contiguous and a merging wave reads back the same lanes' values.
+    // Split request.  An item's partial is HP x 512 normalised values in
+    // bf16, in 1 KB block pairs, inside a slot of HP x 512 fp32: block
+    // (h, cb, g) stands for columns 32 cb + 8 g + 4 (l / 32) .. +3 of head
+    // 32 h + l % 32 in lane l (the accumulator layout), and block pair
+    // (h, cb, p) at byte (32 h + 2 cb + p) KB holds, in lane l's 16 bytes,
+    // that lane's values of blocks (h, cb, 2p) and (h, cb, 2p + 1), so that
+    // each store instruction writes 1 KB contiguous and a merging wave reads
+    // back the same lanes' values.  (bf16 rounding of a normalised partial,
+    // 2^-9 relative, is below the output's own bf16 rounding.)
     // Partials are written and read with sc1 accesses, which are coherent at
     // agent scope (the form that relaxed agent-scope atomics take), so items
     // on different XCDs exchange them without writing back or invalidating
@@ -1091,11 +1095,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
-    // this lane's 16 bytes of block (h, CPW w + c, g): slab + (64 h + 4 c + g)
-    // KB; pad[h] moves the lanes of padding heads past the resource, so their
-    // stores and loads are dropped without a branch
-    const uint32_t slab = uint32_t(4 * CPW * w) * 1024 + uint32_t(lane_e) * 16;
-    const uint32_t slabp = uint32_t(2 * CPW * w) * 1024 + uint32_t(lane_e) * 16;  // bf16 half partials
+    // this lane's 16 bytes of block pair (h, CPW w + c, pp): slabp + (32 h +
+    // 2 c + pp) KB; pad[h] moves the lanes of padding heads past the
+    // resource, so their stores and loads are dropped without a branch
+    const uint32_t slabp = uint32_t(2 * CPW * w) * 1024 + uint32_t(lane_e) * 16;
     uint32_t pad[NW];
 #pragma unroll
     for (int h = 0; h < NW; ++h) pad[h] = (h * 32 + hl_e < a.H) ? 0u : 0x40000000u;
@@ -1106,11 +1109,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v4;
+          for (int pp = 0; pp < 2; ++pp) {
+            bf16x8 v8;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v4[r] = o[h * CPW + c][4 * g + r] * inv[h];
-            __builtin_amdgcn_raw_buffer_store_b128(v4, pr, slab + pad[h] + (64 * h + 4 * c + g) * 1024, 0, kSc1);
+            for (int r = 0; r < 8; ++r) v8[r] = (__bf16)(o[h * CPW + c][8 * pp + r] * inv[h]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v8), pr,
+                                                   slabp + pad[h] + (32 * h + 2 * c + pp) * 1024, 0, kSc1);
           }
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), plse_r, uint32_t(it * HP + head_e) * 4, 0, kSc1);
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): this lane's partial is out
@@ -1313,7 +1317,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     const int head_m = w * 32 + (lane_m & 31);
     const int hi_m = lane_m >> 5;
     // lanes of padding heads read past the resource (zeros, no traffic)
-    const uint32_t moff = (head_m < a.H ? uint32_t(lane_m) * 16 : 0x40000000u) + uint32_t(cb0) * 4096;
+    const uint32_t moff = (head_m < a.H ? uint32_t(lane_m) * 16 : 0x40000000u) + uint32_t(cb0) * 2048;
     auto slot_of = [&](int s) { return (s < rq[1]) ? rq[0] + s : rq[2]; };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
@@ -1348,22 +1352,25 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     auto weight = [&](int s) {
       return (in_lds ? wsl[32 * s] : __builtin_amdgcn_exp2f(lse_of(slot_of(s)) - mlse)) * inv;
     };
-    // 4 kCb KB of each item per wave, 32 loads in flight at a time
-    constexpr int kNB = 4 * kCb;           // 1 KB blocks per item
-    constexpr int kBatch = 32 / kNB;       // items per batch of loads
+    // 2 kCb KB of each item per wave (block pairs 2 c + pp of head block w,
+    // at 32 w KB of the item's slot), 32 loads in flight at a time
+    constexpr int kNB = 4 * kCb;           // fp32 accumulator blocks
+    constexpr int kNP = 2 * kCb;           // 1 KB block pairs per item
+    constexpr int kBatch = 32 / kNP;       // items per batch of loads
     f32x4 acc[kNB] = {};
     for (int s0 = 0; s0 < cnt; s0 += kBatch) {
-      f32x4 x[kBatch][kNB];
+      i32x4 x[kBatch][kNP];
       float wt[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (s0 + j < cnt) {
           const int slot = slot_of(s0 + j);
           const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)(a.part_o + (size_t(slot) * HP + w * 32) * kDV), (short)0, kWaveBytesM, 0x00020000);
+              (void*)(reinterpret_cast<char*>(a.part_o + size_t(slot) * HP * kDV) + w * kWaveBytesM), (short)0,
+              kWaveBytesM, 0x00020000);
 #pragma unroll
-          for (int g = 0; g < kNB; ++g)
-            x[j][g] = __builtin_amdgcn_raw_buffer_load_b128(pr, moff + g * 1024, 0, kSc1);
+          for (int pq = 0; pq < kNP; ++pq)
+            x[j][pq] = __builtin_amdgcn_raw_buffer_load_b128(pr, moff + pq * 1024, 0, kSc1);
           wt[j] = weight(s0 + j);
         }
       }
@@ -1371,9 +1378,13 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
       for (int j = 0; j < kBatch; ++j)
         if (s0 + j < cnt)
 #pragma unroll
-          for (int g = 0; g < kNB; ++g)
+          for (int pq = 0; pq < kNP; ++pq) {
+            const bf16x8 v8 = __builtin_bit_cast(bf16x8, x[j][pq]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(wt[j], x[j][g][r], acc[g][r]);
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[2 * pq + k][r] = fmaf(wt[j], (float)v8[4 * k + r], acc[2 * pq + k][r]);
+          }
     }
     {
       // stores of heads >= H fall outside the resources

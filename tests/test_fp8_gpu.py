@@ -141,9 +141,14 @@ def test_fp8_matches_bf16_decode_of_dequantised_cache(lens, H, BS):
     Every score product and every weighted-sum term is the same on both
     paths; only the order in which the score MFMAs add up the 576 products
     differs (the fp8 path reads two k-steps of 16 bytes at a time), which
-    moves a score by a few fp32 ulps.  So lse agrees to 1e-5 and each output
-    to one bf16 rounding step, 2^-7 of its magnitude (plus 1e-4 where terms
-    cancel)."""
+    moves a score by a few fp32 ulps.  So lse agrees to 1e-5.  An output
+    agrees to one bf16 rounding step of its own magnitude, 2^-7 |out|, plus,
+    for a split request, one bf16 step of the split partials it merges:
+    each path rounds its own partials to bf16, and two nearly equal values
+    may round one step apart, 2^-7 |o_s|.  A normalised partial is a convex
+    combination of the request's V rows, so |o_s| <= max_t |V[t, col]| over
+    the request's tokens; 1e-4 covers the fp32 differences where terms
+    cancel."""
     w = _gpu(wl.make_custom(lens, H=H, BS=BS, seed=12))
     c8 = wl.fp8_cache(w.cache, 0.0625)
     deq = (c8.view(torch.float8_e4m3fn).float() * 0.0625).to(torch.bfloat16)
@@ -157,9 +162,18 @@ def test_fp8_matches_bf16_decode_of_dequantised_cache(lens, H, BS):
     d_out = np.abs(o8 - ob)
     fin = np.isfinite(lb)  # empty requests: lse = -inf on both paths
     d_lse = np.abs(l8[fin] - lb[fin])
+    # max_t |V[t, col]| over each request's tokens, from the dequantised rows
+    vmax = np.zeros((w.B, 1, 512), dtype=np.float32)
+    rows = deq.float().cpu().numpy()
+    table = w.block_table.cpu().numpy()
+    for b, L in enumerate(lens):
+        t = np.arange(int(L))
+        if len(t):
+            v = rows[table[b, t // BS], t % BS, :512]
+            vmax[b, 0] = np.abs(v).max(axis=0)
     _say(f"[fp8] vs bf16 of the dequantised cache: max |d out| {d_out.max():.3g}, "
          f"equal {np.mean(o8 == ob):.4f}, max |d lse| {d_lse.max():.3g}")
-    assert np.all(d_out <= 2.0 ** -7 * np.maximum(np.abs(o8), np.abs(ob)) + 1e-4)
+    assert np.all(d_out <= 2.0 ** -7 * (np.maximum(np.abs(o8), np.abs(ob)) + vmax) + 1e-4)
     assert np.array_equal(np.isneginf(l8), np.isneginf(lb)) and np.all(np.isneginf(lb[~fin]))
     assert np.all(d_lse <= 1e-5 * np.maximum(1.0, np.abs(lb[fin])))
 
