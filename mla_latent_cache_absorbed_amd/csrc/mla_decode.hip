@@ -1091,7 +1091,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_attend_kernel(AttendArgs a) {
     // item; wider splits by merge units once the item queue is empty.
     auto part_rsrc = [&](int slot) {
       return __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.part_o + size_t(slot) * HP * kDV), (short)0, HP * kDV * 4, 0x00020000);
+          (void*)(a.part_o + size_t(slot) * HP * kDV), (short)0, HP * kDV * 2, 0x00020000);
     };
     const __amdgpu_buffer_rsrc_t plse_r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.part_lse, (short)0, 0x7ffffff0, 0x00020000);
