@@ -2035,6 +2035,9 @@ __device__ __forceinline__ Scan4 block_scan4(int4 v, int4* s_scan) {
 // first, then the full chunks of every other request, then their last
 // (shorter) chunks, then one item per empty request.  With at most kPlanLens
 // requests the (clamped) lengths are read from memory once and kept in LDS.
+// kSingle: B <= kPlanThreads, placed in one pass (the instantiation holds
+// only that path, so none of the multi-pass code's registers are live).
+template <bool kSingle>
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     const int32_t* __restrict__ seq_lens, int B, int M, int lgBS, int n_slots, int forced,
     int ovh, int cap, int units_per_req, int nx, int32_t* __restrict__ hdr, int4* __restrict__ req,
@@ -2046,7 +2049,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
   __shared__ __attribute__((aligned(16))) float s_m[kPlanLens];
   const int tid = threadIdx.x;
   const int Lmax = M << lgBS;
-  const bool resident = B <= kPlanLens;
+  const bool resident = kSingle || B <= kPlanLens;
   auto clamp_len = [&](int L0) { return min(max(L0, 0), Lmax); };
   // lengths of requests b0 .. b0 + nb - 1 into LDS, padded with -1 to a
   // multiple of 4, and ceil(L / 32) as floats, padded with 0; returns this
@@ -2199,7 +2202,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
     return make_int4(pair ? 0 : nf0, pair ? 0 : nr0, (b < B && L == 0) ? 1 : 0, pair ? 1 : 0);
   };
 
-  if (resident && B <= kPlanThreads) {
+  if (kSingle || (resident && B <= kPlanThreads)) {
     // 2) one pass: a single scan gives every request's prefix and the
     //    totals.  With B <= 1024 every count and prefix fits 16 bits, so
     //    the empty and widely-split counts share a word, as do the pair
@@ -2221,7 +2224,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(
                                  (sc.incl.w & 0xffff) - c.w);
       place(b, L, nf0, nr0, pre, (sc.incl.z >> 16) - nbg);
     }
-  } else {
+  } else if constexpr (!kSingle) {
     // 2) totals: the items of pairs and of all other requests, empty
     //    requests, widely split requests and the range-check bits
     int4 loc = make_int4(0, 0, 0, 0);
@@ -2454,13 +2457,17 @@ mla_status launch_plan(const int32_t* seq_lens, int32_t B, int32_t H, int32_t M,
   // the wide kernels take their first items in workgroup order, so pairs
   // placed nx apart land on one XCD; the narrow kernel's workers do not
   const int nx = v.nw ? nxcd : 1;
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st,
-                     seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.workers_per_cu,
-                     (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req, nx,
-                     reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
-                     reinterpret_cast<int32_t*>(ws + L.ctr_off),
-                     reinterpret_cast<int32_t*>(ws + L.big_off),
-                     reinterpret_cast<int4*>(ws + L.item_off));
+  auto launch_plan = [&](auto single_c) {
+    hipLaunchKernelGGL((mla_plan_kernel<decltype(single_c)::value>), dim3(1), dim3(kPlanThreads), 0, st,
+                       seq_lens, (int)B, (int)M, ilog2_exact(BS), ncu * v.workers_per_cu,
+                       (int)chunk_tokens, item_overhead_tokens(H), L.cap, v.units_per_req, nx,
+                       reinterpret_cast<int32_t*>(ws), reinterpret_cast<int4*>(ws + L.req_off),
+                       reinterpret_cast<int32_t*>(ws + L.ctr_off),
+                       reinterpret_cast<int32_t*>(ws + L.big_off),
+                       reinterpret_cast<int4*>(ws + L.item_off));
+  };
+  if (B <= kPlanThreads) launch_plan(BoolC<true>{});
+  else launch_plan(BoolC<false>{});
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
