@@ -112,6 +112,22 @@ def test_forced_splits(H, chunk):
     assert np.array_equal(lse2.cpu().numpy(), lse)
 
 
+@pytest.mark.parametrize("H,lens", [(128, [32 * 400, 37]), (48, [32 * 600]), (16, [32 * 400, 37])])
+def test_splits_wider_than_the_staged_weights(H, lens):
+    """A request split into more items than the merge units keep weights for
+    in LDS (288 at 128 heads and at 32 or fewer, 576 at 33 to 64): the units
+    then recompute every item's weight from its log-sum-exp.  Forced 32-token
+    chunks; the plan's cap (B * items per request <= B + 1024) bounds B."""
+    w = _to_gpu(wl.make_custom(lens, H=H, BS=64, seed=21, poison_unused=True))
+    ws = mla.Workspace(w.B, w.H, w.M, w.BS)
+    out, lse = _run(w, chunk_tokens=32, ws=ws)
+    ro, rl = _oracle(w)
+    _assert_parity(out, lse, ro, rl, f"H={H} lens={lens} chunk=32")
+    hdr = ws.header()
+    assert hdr[0] == sum(-(-L // 32) for L in lens), hdr
+    assert hdr[3] == 0 and hdr[6] == 0 and ws.check_flags() == 0, hdr
+
+
 def test_more_requests_than_the_plan_stages():
     """B > 4096: the plan reads lengths from memory in passes instead of
     keeping them in LDS (auto and forced chunk sizes), with empty, short and a
