@@ -86,6 +86,14 @@ def test_fp8_forced_splits(H, chunk, BS):
     _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"H={H} chunk={chunk}", chunk=chunk)
 
 
+@pytest.mark.parametrize("H,lens", [(128, [32 * 400, 37]), (48, [32 * 600]), (16, [32 * 400, 37])])
+def test_fp8_splits_wider_than_the_staged_weights(H, lens):
+    """As for the bf16 cache: more items than the merge units keep weights
+    for in LDS, so every weight is recomputed from its log-sum-exp."""
+    w = _gpu(wl.make_custom(lens, H=H, BS=64, seed=22, poison_unused=True))
+    _check(w, wl.fp8_cache(w.cache), wl.DEFAULT_KV_SCALE, f"H={H} lens={lens} chunk=32", chunk=32)
+
+
 @pytest.mark.parametrize("H", [128, 16])
 def test_fp8_large_score_range_redo_path(H):
     """A key far larger than the rest late in a request forces the redo path."""
