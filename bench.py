@@ -257,16 +257,17 @@ def stream_read_record(gib: int = 4, reps: int = 5) -> dict:
 def mfma_loop_record(iters: int = 20000, reps: int = 5) -> dict:
     """bf16 MFMA rate this GPU attains: the probe library's loop of
     independent v_mfma_f32_32x32x16_bf16 on random operands, with 1 and 2
-    workgroups of 4 waves per CU (one or two waves per SIMD), HIP events
-    around `reps` launches of each; TFLOP/s and the fraction of the 2.5
-    PFLOP/s dense bf16 peak."""
+    workgroups of 4 waves per CU (one or two waves per SIMD), and the same
+    loop on v_mfma_f32_16x16x32_bf16 at one wave per SIMD; HIP events around
+    `reps` launches of each; TFLOP/s and the fraction of the 2.5 PFLOP/s
+    dense bf16 peak (best of the 32x32x16 runs)."""
     import ctypes
     import torch
     from mla_latent_cache_absorbed_amd import build as _b
     lib = ctypes.CDLL(_b.PROBE_LIB)
     lib.mla_probe_mfma.restype = ctypes.c_double
-    lib.mla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.mla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.mla_probe_sink_bytes.restype = ctypes.c_size_t
     lib.mla_probe_sink_bytes.argtypes = [ctypes.c_int32]
     dev = torch.device("cuda")
@@ -278,26 +279,28 @@ def mfma_loop_record(iters: int = 20000, reps: int = 5) -> dict:
     clk = torch.zeros(2, dtype=torch.int64, device=dev)
     st = torch.cuda.current_stream()
     runs, ghz, busy = {}, {}, {}
-    for wpc in (1, 2):
-        fl = lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(), None, st.cuda_stream)
+    for shape, wpc in ((32, 1), (32, 2), (16, 1)):
+        key = f"wg{wpc}" if shape == 32 else f"16x16x32_wg{wpc}"
+        fl = lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, shape, sink.data_ptr(), None, st.cuda_stream)
         if fl <= 0:
             raise RuntimeError("MFMA probe failed to launch")
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(st)
         for r in range(reps):
-            lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, sink.data_ptr(),
+            lib.mla_probe_mfma(ab.data_ptr(), iters, wpc, shape, sink.data_ptr(),
                                clk.data_ptr() if r == reps - 1 else None, st.cuda_stream)
         e1.record(st)
         torch.cuda.synchronize()
-        runs[f"wg{wpc}"] = fl / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+        runs[key] = fl / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
         cyc, ticks = (int(v) for v in clk.tolist())
         # core clock of the first wave's loop, and the share of its cycles
-        # its MFMA pipe was busy (32 cycles per MFMA, 2 x 4 per round)
-        ghz[f"wg{wpc}"] = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else None
-        busy[f"wg{wpc}"] = wpc * iters * 8 * 32 / cyc if cyc > 0 else None
+        # its MFMA pipe was busy if each 32,768 flop take 32 cycles (the
+        # 32x32x16 rate; 2 x 4 of them per round)
+        ghz[key] = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else None
+        busy[key] = wpc * iters * 8 * 32 / cyc if cyc > 0 else None
     del ab, sink, clk
-    best = max(runs.values())
+    best = max(v for k, v in runs.items() if not k.startswith("16x16x32"))
     return {"tflops": runs, "best_tflops": best, "frac_of_peak": best / MFMA_BF16_PEAK_TFS,
             "core_clock_ghz": ghz, "simd_mfma_busy": busy}
 

@@ -1,7 +1,7 @@
 // Read-only streaming probes of HBM bandwidth on gfx950, used by the
 // benchmark to state the read bandwidth this GPU attains next to its 8 TB/s
-// peak, and an MFMA loop that states the bf16 matrix rate it attains next to
-// its 2.5 PFLOP/s peak.  Not part of the decode path: built as its own small
+// peak, and MFMA loops that state the bf16 matrix rate it attains next to
+// its 2.5 PFLOP/s peak, for the 32x32x16 and 16x16x32 shapes.  Not part of the decode path: built as its own small
 // library.
 //
 //   mode 0  plain 16-byte global loads into registers, eight in flight per
@@ -97,41 +97,67 @@ __global__ __launch_bounds__(kThreads) void read_lds(const char* __restrict__ p,
   sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = acc;
 }
 
-// MFMA loop: every wave runs `iters` rounds of 2 kChains
-// v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 bf16 products into fp32, 32,768
-// flop each) into kChains independent accumulators, on operands loaded once
-// from `ab` (random bf16, so the products toggle like real data): two A
-// fragments, and the two B fragments in turn; one word per lane goes to the
-// sink so that nothing is optimised away.
+// MFMA loop: every wave runs `iters` rounds of 262,144 flop of bf16 MFMAs
+// on operands loaded once from `ab` (random bf16, so the products toggle
+// like real data): two A fragments, and the two B fragments in turn.
+// kShape 32: 2 x 4 v_mfma_f32_32x32x16_bf16 (32,768 flop each) into four
+// independent accumulators; kShape 16: 2 x 8 v_mfma_f32_16x16x32_bf16
+// (16,384 flop each) into eight.  One word per lane goes to the sink so that
+// nothing is optimised away.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int kChains = 4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr double kRoundFlop = 8 * 32768.0;  // flop per wave and round, both shapes
 
-template <int kWpc>
+template <int kShape>
+__device__ __forceinline__ float mfma_rounds(bf16x8 a0, bf16x8 a1, bf16x8 b0, bf16x8 b1, int iters) {
+  float s = 0.0f;
+  if constexpr (kShape == 32) {
+    f32x16 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((c & 1) ? a1 : a0, b0, acc[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((c & 1) ? a1 : a0, b1, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += acc[c][r];
+  } else {
+    f32x4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((c & 1) ? a1 : a0, b0, acc[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((c & 1) ? a1 : a0, b1, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += acc[c][r];
+  }
+  return s;
+}
+
+template <int kWpc, int kShape>
 __global__ __launch_bounds__(kThreads) void mfma_loop(const bf16x8* __restrict__ ab, int iters,
                                                      float* __restrict__ sink, uint64_t* __restrict__ clk) {
   __shared__ uint32_t occ[occ_words<kWpc>()];
   const int lane = threadIdx.x & 63;
   const bf16x8 a0 = ab[lane], a1 = ab[64 + lane], b0 = ab[128 + lane], b1 = ab[192 + lane];
-  f32x16 acc[kChains];
-#pragma unroll
-  for (int c = 0; c < kChains; ++c) acc[c] = f32x16{};
   // operands in registers before the clocks start
   __builtin_amdgcn_s_waitcnt(0);
   const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
-  for (int i = 0; i < iters; ++i) {
-#pragma unroll
-    for (int c = 0; c < kChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((c & 1) ? a1 : a0, b0, acc[c], 0, 0, 0);
-#pragma unroll
-    for (int c = 0; c < kChains; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((c & 1) ? a1 : a0, b1, acc[c], 0, 0, 0);
-  }
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kChains; ++c)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  const float s = mfma_rounds<kShape>(a0, a1, b0, b1, iters);
   // the sum depends on every accumulator, so the clocks below follow the loop
   sink[size_t(blockIdx.x) * kThreads + threadIdx.x] = __uint_as_float(through_lds(occ, __float_as_uint(s)));
   __builtin_amdgcn_s_waitcnt(0);
@@ -192,34 +218,41 @@ size_t mla_probe_stream_read(const void* buf, size_t bytes, int32_t mode, int32_
   return n_iter * grid * kStep;
 }
 
-// Runs the MFMA loop with `wg_per_cu` (1, 2 or 4) workgroups of 256 threads (4 waves)
+// Runs the MFMA loop of `shape` (32: 32x32x16, 16: 16x16x32) with
+// `wg_per_cu` (1, 2 or 4) workgroups of 256 threads (4 waves)
 // per compute unit, `iters` rounds each, on `stream`.  `ab` is a device
 // buffer of at least 256 x 16 bytes of bf16 operands; `sink` as for the
 // stream probe; `clk`, if not null, a device buffer of two uint64 that gets
 // the core-clock cycles and the 100 MHz real-time ticks of the first wave's
 // loop.  Returns the flops of the launch, or 0 on a bad argument or launch
 // failure.
-double mla_probe_mfma(const void* ab, int32_t iters, int32_t wg_per_cu, void* sink, void* clk,
+double mla_probe_mfma(const void* ab, int32_t iters, int32_t wg_per_cu, int32_t shape, void* sink, void* clk,
                       void* stream) {
-  if (!ab || !sink || iters < 1 || !(wg_per_cu == 1 || wg_per_cu == 2 || wg_per_cu == 4)) return 0.0;
+  if (!ab || !sink || iters < 1 || !(wg_per_cu == 1 || wg_per_cu == 2 || wg_per_cu == 4) ||
+      !(shape == 32 || shape == 16))
+    return 0.0;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0.0;
   const size_t grid = size_t(ncu) * wg_per_cu;
-  auto launch = [&](auto wpc_c) {
-    constexpr int W = decltype(wpc_c)::value;
-    hipLaunchKernelGGL((mfma_loop<W>), dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+  auto launch = [&](auto wpc_c, auto shape_c) {
+    constexpr int W = decltype(wpc_c)::value, SH = decltype(shape_c)::value;
+    hipLaunchKernelGGL((mfma_loop<W, SH>), dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                        static_cast<const bf16x8*>(ab), iters, static_cast<float*>(sink),
                        static_cast<uint64_t*>(clk));
   };
+  auto by_shape = [&](auto wpc_c) {
+    if (shape == 32) launch(wpc_c, std::integral_constant<int, 32>{});
+    else launch(wpc_c, std::integral_constant<int, 16>{});
+  };
   switch (wg_per_cu) {
-    case 1: launch(std::integral_constant<int, 1>{}); break;
-    case 2: launch(std::integral_constant<int, 2>{}); break;
-    default: launch(std::integral_constant<int, 4>{}); break;
+    case 1: by_shape(std::integral_constant<int, 1>{}); break;
+    case 2: by_shape(std::integral_constant<int, 2>{}); break;
+    default: by_shape(std::integral_constant<int, 4>{}); break;
   }
   if (hipGetLastError() != hipSuccess) return 0.0;
-  return double(grid) * (kThreads / 64) * double(iters) * 2 * kChains * 32768.0;
+  return double(grid) * (kThreads / 64) * double(iters) * kRoundFlop;
 }
 
 }  // extern "C"
